@@ -1,0 +1,314 @@
+"""Pins that tie the fp64 oracle to something other than itself.
+
+Each ``pin_*`` takes the oracle module (``oracle.fp64``) and raises
+AssertionError on a violation, so the same pins can be run against planted
+mutants of the oracle (tests/test_oracle_mutants.py).
+
+The pages (Flash-KMeans paper page, abstract; the Hacker News article,
+sections 論文の要点 / Flash-KMeans が変える点) print no worked example and no
+numbers for k-means itself, so every pin comes from the mathematics of the
+Lloyd iteration: exact rational brute force, closed forms, planted mixtures,
+invariants and textbook library routines.
+"""
+
+from __future__ import annotations
+
+from fractions import Fraction as F
+
+import numpy as np
+import torch
+
+import datagen
+
+# ---------------------------------------------------------------- rounding
+
+
+_SPECS = {"fp32": (24, -126, 127), "fp16": (11, -14, 15), "bf16": (8, -126, 127)}
+
+
+def frac_round(q: F, fmt: str) -> F:
+    """Exact round-to-nearest-even of a rational into a binary format,
+    written independently of the oracle (integer arithmetic on Fractions)."""
+    if fmt == "fp64":
+        return q
+    p, emin, emax = _SPECS[fmt]
+    if q == 0:
+        return F(0)
+    s = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while F(2) ** e > a:
+        e -= 1
+    while F(2) ** (e + 1) <= a:
+        e += 1
+    qe = max(e, emin) - p + 1
+    scaled = a / (F(2) ** qe)
+    fl = scaled.numerator // scaled.denominator
+    rem = scaled - fl
+    if rem > F(1, 2) or (rem == F(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * F(2) ** qe
+    big = (2 - F(2) ** (1 - p)) * F(2) ** emax
+    if r > big:
+        raise OverflowError
+    return s * r
+
+
+def pin_rounding(L):
+    rng = np.random.default_rng(7)
+    # log-uniform magnitudes over the normal and subnormal ranges of each format
+    for fmt, lo, hi in (("fp32", -140, 120), ("fp16", -24, 15), ("bf16", -133, 120)):
+        x = np.ldexp(rng.uniform(1, 2, 20000), rng.integers(lo, hi, 20000)) * rng.choice([-1, 1], 20000)
+        # exact half-way points between neighbours (the tie rule decides them)
+        p = _SPECS[fmt][0]
+        e = rng.integers(max(lo, -14 if fmt == "fp16" else -126), hi - 1, 4000)
+        m = rng.integers(1 << (p - 1), 1 << p, 4000)
+        half = np.ldexp(m.astype(np.float64) + 0.5, e - p + 1)
+        x = np.concatenate([x, half, -half, [0.0, -0.0]])
+        got = L.round_to_format(x, fmt)
+        if fmt == "fp32":
+            ref = x.astype(np.float32).astype(np.float64)
+        elif fmt == "fp16":
+            ref = x.astype(np.float16).astype(np.float64)
+        else:
+            # bf16 reference: torch's float32 -> bfloat16 conversion (round to
+            # nearest even) on values that are exact in fp32
+            x32 = x.astype(np.float32)
+            x = x32.astype(np.float64)
+            got = L.round_to_format(x, fmt)
+            ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+        assert np.array_equal(got, ref), (fmt, x[got != ref][:5], got[got != ref][:5], ref[got != ref][:5])
+    # exact rational rounding of a few awkward fp64 values
+    for v in (1.0 + 2.0 ** -9, 1.0 + 3 * 2.0 ** -9, 255.5, 1.0 / 3.0, -2.0 ** -130, 3.3895e38):
+        for fmt in ("bf16", "fp16", "fp32"):
+            try:
+                want = float(frac_round(F(v), fmt))
+            except OverflowError:
+                want = float("inf") if v > 0 else float("-inf")
+            got = float(L.round_to_format(np.array([v]), fmt)[0])
+            assert got == want, (v, fmt, got, want)
+
+
+def pin_decode(L):
+    rng = np.random.default_rng(3)
+    v = torch.from_numpy(rng.standard_normal(4096).astype(np.float32) * 50).to(torch.bfloat16)
+    bits = v.view(torch.int16).numpy().view(np.uint16)
+    got = L.decode(bits, "bf16")
+    assert np.array_equal(got, v.to(torch.float32).numpy().astype(np.float64))
+    h = (rng.standard_normal(4096) * 50).astype(np.float16)
+    assert np.array_equal(L.decode(h.view(np.uint16), "fp16"), h.astype(np.float64))
+    assert np.array_equal(L.decode(h, "fp16"), h.astype(np.float64))
+
+
+# ------------------------------------------------- exact rational brute force
+
+
+def bf_lloyd(X, C0, iters, fmt):
+    """Lloyd's iteration in exact rational arithmetic (Fractions)."""
+    X = [[F(float(v)) for v in row] for row in X]
+    C = [[F(float(v)) for v in row] for row in C0]
+    K = len(C)
+    hist = []
+    for _ in range(iters):
+        Ch = [[frac_round(c, fmt) for c in row] for row in C]
+        labels, J = [], F(0)
+        for x in X:
+            ds = [sum((a - b) ** 2 for a, b in zip(x, c)) for c in Ch]
+            m = min(ds)
+            labels.append(ds.index(m))  # first minimum: lowest index wins ties
+            J += m
+        hist.append(J)
+        counts = [0] * K
+        sums = [[F(0)] * len(X[0]) for _ in range(K)]
+        for x, lab in zip(X, labels):
+            counts[lab] += 1
+            sums[lab] = [s + a for s, a in zip(sums[lab], x)]
+        C = [[s / counts[k] for s in sums[k]] if counts[k] else C[k] for k in range(K)]
+    return labels, C, hist, counts
+
+
+def _dyadic_problem(rng, n, k, d, fmt):
+    X = rng.integers(-16, 17, size=(n, d)).astype(np.float64) / 4.0
+    C0 = X[rng.choice(n, size=k, replace=False)].copy()
+    if k >= 3:
+        C0[k - 1] = C0[1]            # duplicate centroid: the higher index must stay empty
+    if fmt == "fp32":
+        X = X.astype(np.float32).astype(np.float64)
+    return X, C0
+
+
+def pin_bruteforce(L):
+    rng = np.random.default_rng(11)
+    cases = [("fp64", 1), ("bf16", 4), ("fp16", 4), ("fp32", 3), ("bf16", 1)]
+    for ci, (fmt, iters) in enumerate(cases):
+        for rep in range(3):
+            n = int(rng.integers(8, 64))
+            k = int(rng.integers(1, 8))
+            d = int(rng.integers(1, 4))
+            X, C0 = _dyadic_problem(rng, n, k, d, fmt)
+            # plant exact ties: points midway between two distinct centroids
+            if k >= 2 and n >= 4:
+                X[0] = (C0[0] + C0[1]) / 2
+                X[1] = C0[0]
+            labels, C, hist, counts = bf_lloyd(X, C0, iters, fmt)
+            out = L.lloyd(X, fmt, C0, iters)
+            assert np.array_equal(out["labels"], np.array(labels)), (fmt, rep, out["labels"], labels)
+            assert np.array_equal(out["counts"], np.array(counts)), (fmt, rep)
+            Cx = np.array([[float(v) for v in row] for row in C])
+            assert np.allclose(out["C"], Cx, rtol=4e-16, atol=1e-300), (fmt, rep)
+            for hj, bj in zip(out["history"], hist):
+                assert abs(hj - float(bj)) <= 1e-14 * max(1.0, float(bj)), (fmt, rep, hj, float(bj))
+
+
+# ------------------------------------------------------------- closed forms
+
+
+def pin_closed_forms(L):
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((500, 6)) * 3 + 1
+    # K = 1: the centroid is the column mean and the second inertia is
+    # sum ||x||^2 - N ||mean||^2
+    C0 = X[:1].copy()
+    out = L.lloyd(X, "fp64", C0, 2)
+    mean = X.mean(axis=0)
+    assert np.allclose(out["C"][0], mean, rtol=1e-13, atol=1e-13)
+    J1 = float((X * X).sum() - X.shape[0] * (mean @ mean))
+    assert abs(out["history"][1] - J1) <= 1e-10 * J1
+    assert abs(out["history"][0] - float(((X - X[0]) ** 2).sum())) <= 1e-12 * out["history"][0]
+    # K = N, C0 = X with distinct rows: identity labels and zero inertia
+    Xs = X[:40]
+    out = L.lloyd(Xs, "fp64", Xs.copy(), 2)
+    assert np.array_equal(out["labels"], np.arange(40))
+    assert out["inertia"] == 0.0 and np.array_equal(out["C"], Xs)
+    # all rows identical and all centroids equal to them: every label is 0,
+    # the other clusters are empty and keep their previous value
+    Xi = np.tile(np.array([[1.5, -2.0, 0.25]]), (30, 1))
+    Ci = np.tile(Xi[:1], (4, 1))
+    out = L.lloyd(Xi, "bf16", Ci, 2)
+    assert np.array_equal(out["labels"], np.zeros(30)) and list(out["counts"]) == [30, 0, 0, 0]
+    assert np.array_equal(out["C"], Ci) and out["inertia"] == 0.0
+    # duplicate centroid: the higher index is never chosen and keeps its value
+    C2 = X[[3, 7, 7, 9]].copy()
+    labels, _ = L.assign(X, C2)
+    assert not np.any(labels == 2) and np.any(labels == 1)
+    Cn, cnt = L.update(X, labels, C2, 4)
+    assert cnt[2] == 0 and np.array_equal(Cn[2], C2[2])
+    # D = 1 with sorted centroids: labels are non-decreasing in x
+    x1 = np.sort(rng.standard_normal((300, 1)) * 4, axis=0)
+    c1 = np.sort(rng.standard_normal((7, 1)) * 4, axis=0)
+    lab, _ = L.assign(x1, c1)
+    assert np.all(np.diff(lab) >= 0)
+    # known nearest centroid in 1-D by hand
+    lab, dmin = L.assign(np.array([[0.0], [0.9], [2.0], [-5.0]]), np.array([[-1.0], [1.0], [3.0]]))
+    assert list(lab) == [0, 1, 1, 0] and np.allclose(dmin, [1.0, 0.01, 1.0, 16.0])
+
+
+# -------------------------------------------------------- planted mixtures
+
+
+def pin_planted(L):
+    for fmt, seed in (("bf16", 1), ("fp16", 2), ("fp32", 3)):
+        M = 24
+        X, _, comp, _ = datagen.mixture(3000, 16, M, dtype=fmt, center_dist="normal", center_scale=40.0,
+                                        sigma=1.0, weights=None, workload_code=99, seed=seed)
+        X = X[0]
+        comp = comp[0]
+        if fmt == "bf16":
+            Xd = L.decode(X.view(torch.int16).numpy().view(np.uint16), fmt)
+        else:
+            Xd = L.decode(X.numpy(), fmt)
+        rng = np.random.default_rng(seed)
+        order = rng.permutation(M)                 # centroid j starts at a point of component order[j]
+        first = np.array([np.nonzero(comp == c)[0][0] for c in order])
+        C0 = Xd[first]
+        out = L.lloyd(Xd, fmt, C0, 1)
+        inv = np.empty(M, dtype=np.int64)
+        inv[order] = np.arange(M)
+        assert np.array_equal(out["labels"], inv[comp]), fmt
+        means = np.stack([Xd[comp == c].mean(axis=0) for c in order])
+        assert np.allclose(out["C"], means, rtol=1e-14, atol=1e-12), fmt
+        out3 = L.lloyd(Xd, fmt, C0, 3)
+        assert np.array_equal(out3["labels"], inv[comp]), fmt
+        assert np.array_equal(out3["C"], out["C"]), fmt   # exact fixed point
+
+
+# -------------------------------------------------------------- invariants
+
+
+def _onehot_sums(X, labels, k):
+    import scipy.sparse as sp
+    n = X.shape[0]
+    M = sp.csr_matrix((np.ones(n), (labels, np.arange(n))), shape=(k, n))
+    return np.asarray(M @ X)
+
+
+def pin_invariants(L):
+    rng = np.random.default_rng(9)
+    for fmt in ("bf16", "fp16", "fp32", "fp64"):
+        Xt, C0t, _, _ = datagen.mixture(1500, 8, 12, dtype="fp32" if fmt == "fp64" else fmt,
+                                        center_dist="normal", center_scale=2.0, sigma=1.0, weights=None,
+                                        workload_code=98, seed=4, k=12)
+        X = Xt[0].to(torch.float32).numpy().astype(np.float64)
+        C = C0t[0].numpy().astype(np.float64)
+        C[5] = C[4]                    # a duplicate pair forces exact ties / an empty cluster
+        k = C.shape[0]
+        J_prev = None
+        for t in range(6):
+            Ch = L.round_to_format(C, fmt)
+            labels, dmin = L.assign(X, Ch)
+            D2 = L.sq_dist_direct(X, Ch)
+            assert np.array_equal(labels, D2.argmin(axis=1)), (fmt, t)        # lowest-index minimiser
+            assert np.array_equal(dmin, D2[np.arange(X.shape[0]), labels]), (fmt, t)
+            J = L.inertia(dmin)
+            assert abs(J - float(np.sort(D2.min(axis=1)).sum())) <= 1e-12 * J
+            Cn, cnt = L.update(X, labels, C, k)
+            assert cnt.sum() == X.shape[0] and np.array_equal(cnt, np.bincount(labels, minlength=k))
+            S = _onehot_sums(X, labels, k)
+            nz = cnt > 0
+            assert np.allclose(Cn[nz], S[nz] / cnt[nz, None], rtol=1e-13, atol=1e-13), (fmt, t)
+            assert np.array_equal(Cn[~nz], C[~nz]), (fmt, t)
+            if J_prev is not None:
+                # J_t <= J_{t-1} + sum_k n_k ||C_t,k - round(C_t,k)||^2
+                assert J <= J_prev + R + 1e-12 * J_prev, (fmt, t, J, J_prev, R)
+            R = float((cnt * ((Cn - L.round_to_format(Cn, fmt)) ** 2).sum(axis=1)).sum())
+            if fmt == "fp64":
+                assert R == 0.0
+            J_prev = J
+            C = Cn
+        # the labels also match the definition on a shuffled copy of the centroids
+        perm = rng.permutation(k)
+        lab_p, _ = L.assign(X, L.round_to_format(C, fmt)[perm])
+        lab, _ = L.assign(X, L.round_to_format(C, fmt))
+        d_p = L.sq_dist_direct(X, L.round_to_format(C, fmt)[perm])
+        assert np.array_equal(d_p[np.arange(X.shape[0]), lab_p],
+                              L.sq_dist_direct(X, L.round_to_format(C, fmt))[np.arange(X.shape[0]), lab])
+
+
+# --------------------------------------------------------- library routines
+
+
+def pin_libraries(L):
+    from scipy.cluster.vq import vq
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((4000, 12)) * 2
+    C = rng.standard_normal((37, 12)) * 2
+    lab, dmin = L.assign(X, C)
+    code, dist = vq(X, C)
+    assert np.array_equal(lab, code)
+    assert np.allclose(dmin, dist ** 2, rtol=1e-10)
+    try:
+        from sklearn.cluster import KMeans
+    except ImportError:  # pragma: no cover - scikit-learn is in the image
+        return
+    Xt, C0t, _, _ = datagen.mixture(6000, 10, 16, dtype="fp32", center_dist="normal", center_scale=3.0,
+                                    sigma=1.0, weights=None, workload_code=97, seed=8, k=16)
+    X = Xt[0].numpy().astype(np.float64)
+    C0 = C0t[0].numpy().astype(np.float64)
+    out = L.lloyd(X, "fp64", C0, 6)
+    assert np.all(out["counts"] > 0)
+    km = KMeans(n_clusters=16, init=C0, n_init=1, max_iter=6, tol=0.0, algorithm="lloyd").fit(X)
+    assert np.allclose(km.cluster_centers_, out["C"], rtol=1e-10, atol=1e-10)
+
+
+ALL_PINS = [pin_rounding, pin_decode, pin_bruteforce, pin_closed_forms, pin_planted, pin_invariants,
+            pin_libraries]

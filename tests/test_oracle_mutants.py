@@ -1,0 +1,148 @@
+"""Planted mistakes in the oracle must each fail at least one pin (CPU only).
+
+Every mutant is a plausible slip — a dropped term, a wrong sign or tie rule,
+an off-by-one, a wrong divisor, a skipped rounding — applied to the oracle
+with monkeypatch, so the real oracle is untouched.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.fp64 as L
+from tests import oracle_pins as P
+
+_real_assign = L.assign
+_real_update = L.update
+_real_round = L.round_to_format
+_real_decode = L.decode
+_real_lloyd = L.lloyd
+
+
+def _assign_highest_tie(X, Chat, **kw):
+    D = L.sq_dist_direct(X, Chat)
+    lab = D.shape[1] - 1 - np.argmin(D[:, ::-1], axis=1)
+    return lab, D[np.arange(D.shape[0]), lab]
+
+
+def _assign_no_cnorm(X, Chat, **kw):
+    X = np.asarray(X, np.float64)
+    Chat = np.asarray(Chat, np.float64)
+    lab = np.argmin(-2.0 * X @ Chat.T, axis=1)        # dropped ||c||^2
+    return lab, ((X - Chat[lab]) ** 2).sum(1)
+
+
+def _assign_sign(X, Chat, **kw):
+    X = np.asarray(X, np.float64)
+    Chat = np.asarray(Chat, np.float64)
+    D = (X * X).sum(1)[:, None] + 2.0 * X @ Chat.T + (Chat * Chat).sum(1)[None]   # wrong sign
+    lab = np.argmin(D, axis=1)
+    return lab, ((X - Chat[lab]) ** 2).sum(1)
+
+
+def _assign_transposed_dim(X, Chat, **kw):
+    X = np.asarray(X, np.float64)
+    Chat = np.asarray(Chat, np.float64)
+    return _real_assign(X, Chat[:, ::-1])                 # dims reversed on one operand
+
+
+def _update_empty_zero(X, labels, C_prev, k):
+    C, n = _real_update(X, labels, C_prev, k)
+    C[n == 0] = 0.0
+    return C, n
+
+
+def _update_div_n(X, labels, C_prev, k):
+    C, n = _real_update(X, labels, C_prev, k)
+    nz = n > 0
+    C[nz] *= n[nz, None] / max(1, len(labels))
+    return C, n
+
+
+def _update_offbyone(X, labels, C_prev, k):
+    return _real_update(X, np.roll(np.asarray(labels), 1), C_prev, k)
+
+
+def _round_trunc(x, fmt):
+    x = np.asarray(x, np.float64)
+    spec = L.FORMATS[fmt]
+    if spec is None:
+        return x.copy()
+    p, emin, _ = spec
+    _, e = np.frexp(x)
+    q = np.maximum(e - 1, emin) - p + 1
+    return np.ldexp(np.trunc(np.ldexp(x, -q)), q)
+
+
+def _round_half_away(x, fmt):
+    x = np.asarray(x, np.float64)
+    spec = L.FORMATS[fmt]
+    if spec is None:
+        return x.copy()
+    p, emin, _ = spec
+    _, e = np.frexp(x)
+    q = np.maximum(e - 1, emin) - p + 1
+    s = np.ldexp(x, -q)
+    return np.ldexp(np.sign(s) * np.floor(np.abs(s) + 0.5), q)
+
+
+def _round_identity(x, fmt):
+    return np.asarray(x, np.float64).copy()
+
+
+def _decode_bad_shift(a, fmt):
+    a = np.asarray(a)
+    if fmt == "bf16":
+        return (a.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+    return _real_decode(a, fmt)
+
+
+def _lloyd_post_labels(X, fmt, C0, iters):
+    out = _real_lloyd(X, fmt, C0, iters)
+    lab, dmin = _real_assign(X, _real_round(out["C"], fmt))   # extra assignment after the last update
+    out["labels"] = lab
+    out["inertia"] = L.inertia(dmin)
+    return out
+
+
+def _lloyd_unrounded_inertia(X, fmt, C0, iters):
+    out = _real_lloyd(X, fmt, C0, iters)
+    C = np.asarray(C0, np.float64)
+    hist = []
+    for _ in range(iters):
+        lab, _ = _real_assign(X, _real_round(C, fmt))
+        hist.append(L.inertia(((np.asarray(X, np.float64) - C[lab]) ** 2).sum(1)))
+        C, _ = _real_update(X, lab, C, C.shape[0])
+    out["history"] = hist
+    out["inertia"] = hist[-1]
+    return out
+
+
+MUTANTS = {
+    "assign_highest_tie": ("assign", _assign_highest_tie),
+    "assign_no_cnorm": ("assign", _assign_no_cnorm),
+    "assign_sign": ("assign", _assign_sign),
+    "assign_transposed_dim": ("assign", _assign_transposed_dim),
+    "update_empty_zero": ("update", _update_empty_zero),
+    "update_div_n": ("update", _update_div_n),
+    "update_offbyone": ("update", _update_offbyone),
+    "round_trunc": ("round_to_format", _round_trunc),
+    "round_half_away": ("round_to_format", _round_half_away),
+    "round_identity": ("round_to_format", _round_identity),
+    "decode_bad_shift": ("decode", _decode_bad_shift),
+    "lloyd_post_labels": ("lloyd", _lloyd_post_labels),
+    "lloyd_unrounded_inertia": ("lloyd", _lloyd_unrounded_inertia),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(L, attr, fn)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(L)
+        except (AssertionError, ValueError, IndexError, TypeError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"mutant {name} passed every pin"
