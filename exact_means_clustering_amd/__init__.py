@@ -1,0 +1,187 @@
+"""Exact Lloyd k-means on MI355X (gfx950): Python binding of libflashkm.so.
+
+The functions below only marshal torch tensors into the C ABI declared in
+``include/flashkm.h`` (same names without the ``kmeans_`` prefix): every step
+of the computation runs in the library's HIP kernels, on the current torch
+stream.  PyTorch provides device memory and streams, nothing else.  There is
+no CPU fallback: importing raises if the library is missing, and every call
+raises ``KMeansError`` on a non-zero status.
+
+Shapes: X is [N, D] or [B, N, D] (fp32 / fp16 / bf16, CUDA, contiguous);
+centroids are [K, D] or [B, K, D] fp32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "update", "fit", "fit_streamed", "DTYPES"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libflashkm.so"
+
+KM_OK, KM_EINVAL, KM_EUNSUPPORTED, KM_EWORKSPACE, KM_EHIP, KM_ENOMEM = range(6)
+DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+class KMeansError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"flashkm status {status}: {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def _load():
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run `python -m exact_means_clustering_amd.build` "
+                          "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kmeans_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
+    lib.kmeans_workspace_bytes.restype = sz
+    lib.kmeans_assign.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, P, sz, P]
+    lib.kmeans_assign.restype = ctypes.c_int
+    lib.kmeans_update.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, P, sz, P]
+    lib.kmeans_update.restype = ctypes.c_int
+    lib.kmeans_fit.argtypes = [P, i32, i64, i32, i32, P, i32, i32, P, P, P, P, P, sz, P]
+    lib.kmeans_fit.restype = ctypes.c_int
+    lib.kmeans_fit_streamed.argtypes = [P, i32, i64, i32, P, i32, i32, sz, P, P, P, P, P]
+    lib.kmeans_fit_streamed.restype = ctypes.c_int
+    lib.kmeans_last_error.argtypes = []
+    lib.kmeans_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def _check(rc: int):
+    if rc != KM_OK:
+        raise KMeansError(rc, _lib.kmeans_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _shape3(X):
+    if X.dim() == 2:
+        return 1, X.shape[0], X.shape[1]
+    if X.dim() == 3:
+        return X.shape
+    raise ValueError("X must be [N, D] or [B, N, D]")
+
+
+def _dtype(X):
+    try:
+        return DTYPES[X.dtype]
+    except KeyError:
+        raise KMeansError(KM_EUNSUPPORTED, f"unsupported dtype {X.dtype}") from None
+
+
+def _need(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise KMeansError(KM_EINVAL, f"{name} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise KMeansError(KM_EINVAL, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise KMeansError(KM_EINVAL, f"{name} must be {dtype}")
+
+
+def workspace_bytes(N: int, D: int, K: int, B: int = 1, dtype=torch.bfloat16) -> int:
+    dt = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.kmeans_workspace_bytes(N, D, K, B, dt))
+
+
+def _workspace(N, D, K, B, dt, device, ws):
+    need = int(_lib.kmeans_workspace_bytes(N, D, K, B, dt))
+    if need == 0:
+        _check(_lib.kmeans_workspace_bytes(N, D, K, B, dt) or KM_EINVAL)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws
+
+
+def assign(X, C, *, want_min_d2: bool = False, ws=None, stream=None, labels=None):
+    """Assignment stage: returns (labels int32, min_d2 fp32 or None, inertia fp64 [B])."""
+    _need(X, "X")
+    _need(C, "C", torch.float32)
+    B, N, D = _shape3(X)
+    K = C.shape[-2]
+    dt = _dtype(X)
+    lab_shape = X.shape[:-1]
+    labels = torch.empty(lab_shape, dtype=torch.int32, device=X.device) if labels is None else labels
+    md = torch.empty(lab_shape, dtype=torch.float32, device=X.device) if want_min_d2 else None
+    inertia = torch.empty(B, dtype=torch.float64, device=X.device)
+    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    _check(_lib.kmeans_assign(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(labels), _ptr(md), _ptr(inertia),
+                              _ptr(ws), ws.numel(), _stream(stream)))
+    return labels, md, inertia
+
+
+def update(X, labels, C_prev, *, C_new=None, ws=None, stream=None):
+    """Centroid update stage: returns (C_new fp32, counts int32)."""
+    _need(X, "X")
+    _need(labels, "labels", torch.int32)
+    _need(C_prev, "C_prev", torch.float32)
+    B, N, D = _shape3(X)
+    K = C_prev.shape[-2]
+    dt = _dtype(X)
+    C_new = torch.empty_like(C_prev) if C_new is None else C_new
+    counts = torch.empty(C_prev.shape[:-1], dtype=torch.int32, device=X.device)
+    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    _check(_lib.kmeans_update(_ptr(X), dt, N, D, B, _ptr(labels), K, _ptr(C_prev), _ptr(C_new), _ptr(counts),
+                              _ptr(ws), ws.numel(), _stream(stream)))
+    return C_new, counts
+
+
+def fit(X, C0, iters: int, *, history: bool = False, ws=None, stream=None):
+    """Exact Lloyd iteration: returns (labels, C, inertia [B] fp64, history [iters, B] or None)."""
+    _need(X, "X")
+    _need(C0, "C0", torch.float32)
+    B, N, D = _shape3(X)
+    K = C0.shape[-2]
+    dt = _dtype(X)
+    labels = torch.empty(X.shape[:-1], dtype=torch.int32, device=X.device)
+    C = torch.empty_like(C0)
+    inertia = torch.empty(B, dtype=torch.float64, device=X.device)
+    hist = torch.empty((max(1, int(iters)), B), dtype=torch.float64, device=X.device) if history else None
+    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    _check(_lib.kmeans_fit(_ptr(X), dt, N, D, B, _ptr(C0), K, int(iters), _ptr(labels), _ptr(C), _ptr(inertia),
+                           _ptr(hist), _ptr(ws), ws.numel(), _stream(stream)))
+    return labels, C, inertia, hist
+
+
+def fit_streamed(X_host, C0, iters: int, device_x_budget: int, *, history: bool = False, stream=None):
+    """Out-of-core Lloyd iteration over a pinned host tensor X_host [N, D].
+
+    Returns (labels int32 CPU, C fp32 CUDA, inertia float, history list or None)."""
+    if not isinstance(X_host, torch.Tensor) or X_host.is_cuda or not X_host.is_pinned():
+        raise KMeansError(KM_EINVAL, "X_host must be a pinned CPU tensor")
+    if X_host.dim() != 2 or not X_host.is_contiguous():
+        raise KMeansError(KM_EINVAL, "X_host must be a contiguous [N, D] tensor")
+    _need(C0, "C0", torch.float32)
+    N, D = X_host.shape
+    K = C0.shape[-2]
+    dt = _dtype(X_host)
+    labels = torch.empty(N, dtype=torch.int32, pin_memory=True)
+    C = torch.empty_like(C0)
+    inertia = ctypes.c_double(0.0)
+    hist = (ctypes.c_double * max(1, int(iters)))() if history else None
+    _check(_lib.kmeans_fit_streamed(_ptr(X_host), dt, N, D, _ptr(C0), K, int(iters), int(device_x_budget),
+                                    _ptr(labels), _ptr(C), ctypes.byref(inertia),
+                                    hist if hist is not None else None, _stream(stream)))
+    return labels, C, inertia.value, (list(hist) if hist is not None else None)

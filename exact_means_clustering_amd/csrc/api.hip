@@ -1,0 +1,132 @@
+// C ABI of the k-means library: argument validation, workspace carve-up and
+// the stream-ordered Lloyd loop.  See include/flashkm.h for the contract.
+#include "kernels.h"
+#include "workspace.h"
+
+#include "../../include/flashkm.h"
+
+using namespace fkm;
+
+namespace {
+
+int hip_fail(hipError_t e, const char* what) { return fail(KM_EHIP, "%s: %s", what, hipGetErrorString(e)); }
+
+#define KM_HIP(expr, what)                           \
+  do {                                               \
+    hipError_t e_ = (expr);                          \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+bool supported_d(int D) { return D == 16 || D == 32 || D == 64 || D == 128 || D == 256; }
+
+int check_shape(int dtype, int64_t N, int32_t D, int32_t K, int32_t B) {
+  if (dtype != KM_F32 && dtype != KM_F16 && dtype != KM_BF16) return fail(KM_EUNSUPPORTED, "unsupported dtype %d", dtype);
+  if (!supported_d(D)) return fail(KM_EUNSUPPORTED, "unsupported D=%d (supported: 16, 32, 64, 128, 256)", D);
+  if (B < 1) return fail(KM_EINVAL, "B=%d must be >= 1", B);
+  if (K < 1) return fail(KM_EINVAL, "K=%d must be >= 1", K);
+  if (N < K) return fail(KM_EINVAL, "need N >= K (N=%lld, K=%d)", (long long)N, K);
+  if (N * (int64_t)B >= (int64_t)1 << 31) return fail(KM_EINVAL, "B*N must be < 2^31");
+  if ((int64_t)B * K >= (int64_t)1 << 31) return fail(KM_EINVAL, "B*K must be < 2^31");
+  return KM_OK;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, const Layout& L) {
+  if (ws_bytes < L.total)
+    return fail(KM_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, L.total);
+  if (!ws) return fail(KM_EINVAL, "workspace pointer is null");
+  if (((uintptr_t)ws & 255) != 0) return fail(KM_EINVAL, "workspace must be 256-byte aligned");
+  return KM_OK;
+}
+
+// prep + assign (+ inertia) on stream s
+int run_assign(const void* X, int dt, int64_t N, int D, int B, const float* C, int K, int32_t* labels,
+               float* min_d2, double* inertia, double* hist, Work& w, hipStream_t s) {
+  KM_HIP(launch_prep(dt, D, C, w.chat, w.hb, (int64_t)B * K, s), "centroid prep launch");
+  const int pb = assign_pick_pb(dt, D, N, B);
+  KM_HIP(launch_assign(dt, D, pb, X, w.chat, w.hb, N, K, B, labels, min_d2, w.part, s), "assign launch");
+  if (inertia) {
+    const int64_t nwg = (N + assign_rows_per_wg(pb) - 1) / assign_rows_per_wg(pb);
+    KM_HIP(launch_inertia_reduce(w.part, (int)nwg, B, inertia, hist, false, s), "inertia launch");
+  }
+  return KM_OK;
+}
+
+// argsort + offsets + segment means on stream s
+int run_update(const void* X, int dt, int64_t N, int D, int B, const int32_t* labels, int K, const float* C_prev,
+               float* C_new, int32_t* counts, Work& w, hipStream_t s) {
+  const uint32_t* skeys = nullptr;
+  const uint32_t* perm = nullptr;
+  const int64_t n = N * B;
+  const uint32_t nseg = (uint32_t)((int64_t)B * K);
+  KM_HIP(launch_argsort_labels(labels, N, B, K, w.sort, &skeys, &perm, s), "argsort launch");
+  KM_HIP(launch_segment_offsets(skeys, n, nseg, w.off, s), "segment offsets launch");
+  SegOut o{C_prev, C_new, counts ? counts : w.cnt, nullptr, nullptr};
+  KM_HIP(launch_segment_reduce(dt, D, X, perm, skeys, w.off, n, nseg, o, w.seg, s), "segment reduce launch");
+  return KM_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t kmeans_workspace_bytes(int64_t N, int32_t D, int32_t K, int32_t B, int32_t dtype) {
+  if (check_shape(dtype, N, D, K, B) != KM_OK) return 0;
+  return make_layout(N, D, K, B, dtype).total;
+}
+
+int kmeans_assign(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const float* C, int32_t K,
+                  int32_t* labels, float* min_d2, double* inertia, void* ws, size_t ws_bytes, void* stream) {
+  err_buf()[0] = 0;
+  if (int rc = check_shape(dtype, N, D, K, B)) return rc;
+  if (!X || !C || !labels) return fail(KM_EINVAL, "X, C and labels must be non-null");
+  if (!aligned(X, 16) || !aligned(C, 4) || !aligned(labels, 4) || !aligned(min_d2, 4) || !aligned(inertia, 8))
+    return fail(KM_EINVAL, "misaligned pointer (X needs 16 bytes)");
+  const Layout L = make_layout(N, D, K, B, dtype);
+  if (int rc = check_ws(ws, ws_bytes, L)) return rc;
+  Work w = carve(ws, L);
+  return run_assign(X, dtype, N, D, B, C, K, labels, min_d2, inertia, nullptr, w, (hipStream_t)stream);
+}
+
+int kmeans_update(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const int32_t* labels, int32_t K,
+                  const float* C_prev, float* C_new, int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  err_buf()[0] = 0;
+  if (int rc = check_shape(dtype, N, D, K, B)) return rc;
+  if (!X || !labels || !C_prev || !C_new) return fail(KM_EINVAL, "X, labels, C_prev and C_new must be non-null");
+  if (!aligned(X, 16) || !aligned(C_prev, 4) || !aligned(C_new, 4) || !aligned(labels, 4) || !aligned(counts, 4))
+    return fail(KM_EINVAL, "misaligned pointer (X needs 16 bytes)");
+  const Layout L = make_layout(N, D, K, B, dtype);
+  if (int rc = check_ws(ws, ws_bytes, L)) return rc;
+  Work w = carve(ws, L);
+  return run_update(X, dtype, N, D, B, labels, K, C_prev, C_new, counts, w, (hipStream_t)stream);
+}
+
+int kmeans_fit(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const float* C0, int32_t K,
+               int32_t iters, int32_t* labels, float* C_out, double* inertia, double* inertia_hist, void* ws,
+               size_t ws_bytes, void* stream) {
+  err_buf()[0] = 0;
+  if (int rc = check_shape(dtype, N, D, K, B)) return rc;
+  if (iters < 1) return fail(KM_EINVAL, "iters=%d must be >= 1", iters);
+  if (!X || !C0 || !labels || !C_out || !inertia)
+    return fail(KM_EINVAL, "X, C0, labels, C_out and inertia must be non-null");
+  if (!aligned(X, 16) || !aligned(C0, 4) || !aligned(C_out, 4) || !aligned(labels, 4) || !aligned(inertia, 8) ||
+      !aligned(inertia_hist, 8))
+    return fail(KM_EINVAL, "misaligned pointer (X needs 16 bytes)");
+  const Layout L = make_layout(N, D, K, B, dtype);
+  if (int rc = check_ws(ws, ws_bytes, L)) return rc;
+  Work w = carve(ws, L);
+  hipStream_t s = (hipStream_t)stream;
+  for (int t = 0; t < iters; ++t) {
+    const float* Cs = t == 0 ? C0 : C_out;
+    if (int rc = run_assign(X, dtype, N, D, B, Cs, K, labels, nullptr, inertia,
+                            inertia_hist ? inertia_hist + (int64_t)t * B : nullptr, w, s))
+      return rc;
+    if (int rc = run_update(X, dtype, N, D, B, labels, K, Cs, C_out, nullptr, w, s)) return rc;
+  }
+  return KM_OK;
+}
+
+const char* kmeans_last_error(void) { return err_buf(); }
+
+}  // extern "C"

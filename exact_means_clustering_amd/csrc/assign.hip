@@ -1,0 +1,370 @@
+// Assignment stage: centroid preparation and the fused distance + running
+// argmin kernel ("FlashAssign" in the Flash-KMeans paper page, abstract, and
+// the article section "Flash-KMeans が変える点", first point: the distance
+// computation is fused with an online argmin so the N x K distance matrix is
+// never written to memory).
+//
+// Score form.  For a point x and a rounded centroid c,
+//     ||x - c||^2 = ||x||^2 - 2 (x.c - 0.5 ||c||^2),
+// so the nearest centroid maximises s = x.c + hb with hb = -0.5 ||c||^2.
+// The MFMA accumulator is seeded with hb (exact: a power-of-two scaling of
+// the fp32 norm), so the matrix unit produces s directly and the epilogue is
+// a pure running max.
+//
+// Layout.  A 32x32 MFMA output tile has the 32 tile centroids on its rows and
+// 32 points on its columns: lane l owns point l%32 and the 16 centroid rows
+// 8*(r/4) + 4*(l/32) + r%4 (r = accumulator register).  So each lane keeps a
+// private (max, argmax) per point and needs no cross-lane work until the
+// very end, where the two lane halves of a point merge once.
+// The contraction index is permuted so that lane half h feeds the
+// contiguous dims [h*D/2, (h+1)*D/2) of its row: point fragments are then
+// single contiguous loads and stay in registers for the whole sweep, and
+// centroid fragments are contiguous 16-byte LDS reads.
+//
+// Pipeline.  Centroids stream through a double-buffered LDS tile of 64 rows
+// (16-byte chunks XOR-swizzled by row so a 32-row fragment read is free of
+// bank conflicts); the global loads of tile t+1 are issued before the MFMAs
+// of tile t.  One barrier per tile.
+#include "common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+namespace fkm {
+
+// ---------------------------------------------------------------------------
+// centroid preparation: Chat = RNE(C -> dtype), hb = -0.5 ||Chat||^2 (fp32)
+// ---------------------------------------------------------------------------
+template <class T, int D>
+__global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, typename T::raw* __restrict__ Ch,
+                                                   float* __restrict__ hb, int64_t rows) {
+  const int lane = lane_id();
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  constexpr int PER = (D + kWave - 1) / kWave;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int d = lane + kWave * j;
+    if (d < D) {
+      const typename T::raw r = T::from_f32(C[row * D + d]);
+      Ch[row * D + d] = r;
+      const float v = T::to_f32(r);
+      ss += v * v;
+    }
+  }
+  ss = wave_sum_f32(ss);
+  if (lane == 0) hb[row] = -0.5f * ss;
+}
+
+// ---------------------------------------------------------------------------
+// fused assign
+// ---------------------------------------------------------------------------
+constexpr int kTileK = 64;  // centroids per LDS tile
+
+template <class T, int D, int PB>
+struct AssignCfg {
+  static constexpr int RB = D * T::SZ;                 // bytes per row
+  static constexpr int NCH = RB / 16;                  // 16-byte chunks per row
+  static constexpr int HV = NCH / 2;                   // chunks per lane-half fragment
+  static constexpr int STEPS = (D / 2) / T::KPL;       // MFMA steps per 32x32 tile
+  static constexpr int TILE_CH = kTileK * NCH;         // chunks per LDS tile
+  static constexpr int PRE = (TILE_CH + 255) / 256;    // chunks per thread per tile load
+  static constexpr int ROWS = kAssignWaves * 32 * PB;  // points per workgroup
+  static_assert(NCH >= 2 && (NCH & (NCH - 1)) == 0, "row must be a power-of-two number of 16B chunks");
+};
+
+__device__ __forceinline__ float max16(const f32x16& a) {
+  float m0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  float m1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  float m2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
+  float m3 = fmaxf(fmaxf(a[9], a[10]), a[11]);
+  float m4 = fmaxf(fmaxf(a[12], a[13]), a[14]);
+  return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, a[15]));
+}
+
+// Running (max, argmax) update for one lane and one 32-centroid tile.
+// `base` is the centroid index of accumulator register 0 for this lane.
+// Centroid indices grow with the register index, and a tile only replaces
+// the running best on a strictly larger score, so ties keep the lowest index.
+__device__ __forceinline__ void epilogue(const f32x16& acc, float& best, int& bidx, int base) {
+  const float tmax = max16(acc);
+  if (tmax > best) {
+    int r = 15;
+#pragma unroll
+    for (int rr = 14; rr >= 0; --rr)
+      if (acc[rr] == tmax) r = rr;
+    best = tmax;
+    bidx = base + 8 * (r >> 2) + (r & 3);
+  }
+}
+
+template <class T, int D, int PB>
+__global__ __launch_bounds__(256) void assign_kernel(const typename T::raw* __restrict__ X,
+                                                     const typename T::raw* __restrict__ Ch,
+                                                     const float* __restrict__ hb, int64_t N, int K,
+                                                     int32_t* __restrict__ labels, float* __restrict__ min_d2,
+                                                     double* __restrict__ part) {
+  using Cfg = AssignCfg<T, D, PB>;
+  constexpr int NCH = Cfg::NCH, HV = Cfg::HV, STEPS = Cfg::STEPS, PRE = Cfg::PRE;
+  __shared__ uint4 tile[2][Cfg::TILE_CH];
+  __shared__ __align__(16) float tb[2][kTileK];  // read back as float4
+  __shared__ double wsum[kAssignWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int b = blockIdx.y;
+  const typename T::raw* Xb = X + (int64_t)b * N * D;
+  const typename T::raw* Cb = Ch + (int64_t)b * K * D;
+  const float* hbb = hb + (int64_t)b * K;
+  const int64_t p0 = (int64_t)blockIdx.x * Cfg::ROWS + (int64_t)w * (PB * 32);
+
+  // point fragments: lane half h holds dims [h*D/2, (h+1)*D/2) of point col
+  uint4 xf[PB][HV];
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    int64_t n = p0 + p * 32 + col;
+    n = n < N ? n : N - 1;
+    const uint4* src = reinterpret_cast<const uint4*>(Xb + n * D) + h * HV;
+#pragma unroll
+    for (int v = 0; v < HV; ++v) xf[p][v] = src[v];
+  }
+
+  const int ntiles = (K + kTileK - 1) / kTileK;
+  uint4 pre[PRE];
+  float preb = 0.f;
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) {
+      const int q = tid + 256 * i;
+      if (q < Cfg::TILE_CH) {
+        const int m = q / NCH, c = q % NCH;
+        const int k = t * kTileK + m;
+        pre[i] = k < K ? reinterpret_cast<const uint4*>(Cb + (int64_t)k * D)[c] : make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (tid < kTileK) {
+      const int k = t * kTileK + tid;
+      preb = k < K ? hbb[k] : -INFINITY;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) {
+      const int q = tid + 256 * i;
+      if (q < Cfg::TILE_CH) {
+        const int m = q / NCH, c = q % NCH;
+        tile[buf][m * NCH + (c ^ (m & (NCH - 1)))] = pre[i];
+      }
+    }
+    if (tid < kTileK) tb[buf][tid] = preb;
+  };
+
+  float best[PB];
+  int bidx[PB];
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    best[p] = -INFINITY;
+    bidx[p] = 0;
+  }
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+#pragma unroll
+    for (int sb = 0; sb < kTileK / 32; ++sb) {
+      const int m = sb * 32 + col;
+      uint4 af[HV];
+#pragma unroll
+      for (int v = 0; v < HV; ++v) {
+        const int c = h * HV + v;
+        af[v] = tile[buf][m * NCH + (c ^ (m & (NCH - 1)))];
+      }
+      f32x16 bias;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 bq = *reinterpret_cast<const float4*>(&tb[buf][sb * 32 + 8 * q + 4 * h]);
+        bias[4 * q + 0] = bq.x;
+        bias[4 * q + 1] = bq.y;
+        bias[4 * q + 2] = bq.z;
+        bias[4 * q + 3] = bq.w;
+      }
+      const int base = t * kTileK + sb * 32 + 4 * h;
+#pragma unroll
+      for (int p = 0; p < PB; ++p) {
+        f32x16 acc = bias;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) acc = Mfma<T>::step(af, xf[p], st, acc);
+        epilogue(acc, best[p], bidx[p], base);
+      }
+    }
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // merge the two lane halves of each point: larger score, then lower index
+  double wacc = 0.0;
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const float ob = __shfl_xor(best[p], 32);
+    const int oi = __shfl_xor(bidx[p], 32);
+    if (ob > best[p] || (ob == best[p] && oi < bidx[p])) {
+      best[p] = ob;
+      bidx[p] = oi;
+    }
+    // squared distance to the chosen centroid, computed directly (no
+    // cancellation): each half sums its dims, the halves then add.
+    const uint4* cr = reinterpret_cast<const uint4*>(Cb + (int64_t)bidx[p] * D) + h * HV;
+    float part_d = 0.f;
+#pragma unroll
+    for (int v = 0; v < HV; ++v) {
+      float xv[Vec<T>::N], cv[Vec<T>::N];
+      Vec<T>::unpack(xf[p][v], xv);
+      Vec<T>::unpack(cr[v], cv);
+#pragma unroll
+      for (int e = 0; e < Vec<T>::N; ++e) {
+        const float df = xv[e] - cv[e];
+        part_d += df * df;
+      }
+    }
+    const float other = __shfl_xor(part_d, 32);
+    const float d2 = h == 0 ? part_d + other : other + part_d;
+    const int64_t n = p0 + p * 32 + col;
+    if (h == 0 && n < N) {
+      labels[(int64_t)b * N + n] = bidx[p];
+      if (min_d2) min_d2[(int64_t)b * N + n] = d2;
+      wacc += (double)d2;
+    }
+  }
+  wacc = wave_sum_f64(wacc);
+  if (lane == 0) wsum[w] = wacc;
+  __syncthreads();
+  if (tid == 0) part[(int64_t)b * gridDim.x + blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+}
+
+// inertia[b] = fixed-order sum of part[b, :]
+__global__ __launch_bounds__(256) void inertia_reduce_kernel(const double* __restrict__ part, int nwg,
+                                                             double* __restrict__ inertia, double* __restrict__ hist,
+                                                             int accumulate) {
+  __shared__ double ws[4];
+  const int b = blockIdx.x;
+  double v = 0.0;
+  for (int i = threadIdx.x; i < nwg; i += 256) v += part[(int64_t)b * nwg + i];
+  v = wave_sum_f64(v);
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+    if (accumulate) tot += inertia[b];
+    inertia[b] = tot;
+    if (hist) hist[b] = tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+namespace {
+
+template <class T, int D>
+hipError_t prep_t(const float* C, void* Chat, float* hb, int64_t rows, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t grid = (rows + 3) / 4;
+  prep_kernel<T, D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(C, reinterpret_cast<typename T::raw*>(Chat), hb,
+                                                                rows);
+  return hipGetLastError();
+}
+
+template <class T, int D, int PB>
+hipError_t assign_t(const void* X, const void* Chat, const float* hb, int64_t N, int K, int B, int32_t* labels,
+                    float* min_d2, double* part, hipStream_t s) {
+  using Cfg = AssignCfg<T, D, PB>;
+  const int64_t nwg = (N + Cfg::ROWS - 1) / Cfg::ROWS;
+  assign_kernel<T, D, PB><<<dim3((unsigned)nwg, (unsigned)B), dim3(256), 0, s>>>(
+      reinterpret_cast<const typename T::raw*>(X), reinterpret_cast<const typename T::raw*>(Chat), hb, N, K,
+      labels, min_d2, part);
+  return hipGetLastError();
+}
+
+// Register blocking allowed per row size: the point fragments of PB blocks
+// take PB * D * SZ / 8 VGPRs per lane.
+template <class T, int D>
+hipError_t assign_pb(int pb, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
+                     int32_t* labels, float* min_d2, double* part, hipStream_t s) {
+  constexpr int rb = D * T::SZ;
+  if constexpr (rb <= 256) {
+    if (pb >= 4) return assign_t<T, D, 4>(X, Chat, hb, N, K, B, labels, min_d2, part, s);
+  }
+  if constexpr (rb <= 512) {
+    if (pb >= 2) return assign_t<T, D, 2>(X, Chat, hb, N, K, B, labels, min_d2, part, s);
+  }
+  return assign_t<T, D, 1>(X, Chat, hb, N, K, B, labels, min_d2, part, s);
+}
+
+template <template <class, int> class F, class... A>
+hipError_t dispatch_dt_d(int dt, int D, A&&... a) {
+  auto byd = [&](auto tag) -> hipError_t {
+    using T = decltype(tag);
+    switch (D) {
+      case 16: return F<T, 16>::run(a...);
+      case 32: return F<T, 32>::run(a...);
+      case 64: return F<T, 64>::run(a...);
+      case 128: return F<T, 128>::run(a...);
+      case 256: return F<T, 256>::run(a...);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  switch (dt) {
+    case DT_F32: return byd(F32{});
+    case DT_F16: return byd(F16{});
+    case DT_BF16: return byd(BF16{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class T, int D> struct PrepF {
+  static hipError_t run(const float* C, void* Chat, float* hb, int64_t rows, hipStream_t s) {
+    return prep_t<T, D>(C, Chat, hb, rows, s);
+  }
+};
+template <class T, int D> struct AssignF {
+  static hipError_t run(int pb, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
+                        int32_t* labels, float* min_d2, double* part, hipStream_t s) {
+    return assign_pb<T, D>(pb, X, Chat, hb, N, K, B, labels, min_d2, part, s);
+  }
+};
+
+}  // namespace
+
+int assign_pick_pb(int dt, int D, int64_t N, int B) {
+  const int row_bytes = D * dtype_size(dt);
+  const int maxpb = row_bytes <= 256 ? 4 : row_bytes <= 512 ? 2 : 1;
+  // prefer the deepest register blocking that still gives >= 4 workgroups per CU
+  for (int pb = maxpb; pb > 1; pb >>= 1) {
+    const int64_t wgs = (N + assign_rows_per_wg(pb) - 1) / assign_rows_per_wg(pb) * (int64_t)B;
+    if (wgs >= 1024) return pb;
+  }
+  return 1;
+}
+
+hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t rows, hipStream_t s) {
+  return dispatch_dt_d<PrepF>(dt, D, C, Chat, hb, rows, s);
+}
+
+hipError_t launch_assign(int dt, int D, int pb, const void* X, const void* Chat, const float* hb, int64_t N, int K,
+                         int B, int32_t* labels, float* min_d2, double* part, hipStream_t s) {
+  return dispatch_dt_d<AssignF>(dt, D, pb, X, Chat, hb, N, K, B, labels, min_d2, part, s);
+}
+
+hipError_t launch_inertia_reduce(const double* part, int nwg, int B, double* inertia, double* hist, bool accumulate,
+                                 hipStream_t s) {
+  inertia_reduce_kernel<<<dim3((unsigned)B), dim3(256), 0, s>>>(part, nwg, inertia, hist, accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace fkm

@@ -1,0 +1,159 @@
+// Device-side building blocks shared by the k-means kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fkm {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element types.  `raw` is the storage word, KPL the elements one lane feeds
+// to one 32x32 MFMA step, SZ the storage bytes per element.
+// ---------------------------------------------------------------------------
+
+// Round-to-nearest-even fp32 -> bf16 on the bit pattern (bf16 is the upper
+// half of an IEEE binary32; add half an ulp of the kept part, plus one when
+// the kept part is odd, then truncate).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+struct BF16 {
+  using raw = uint16_t;
+  static constexpr int SZ = 2;
+  static constexpr int KPL = 8;
+  __device__ static raw from_f32(float f) { return f32_to_bf16_rne(f); }
+  __device__ static float to_f32(raw r) { return bf16_to_f32(r); }
+  // 8 elements packed in a 16-byte word
+  __device__ static void unpack8(const uint4& v, float* o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+
+struct F16 {
+  using raw = uint16_t;
+  static constexpr int SZ = 2;
+  static constexpr int KPL = 8;
+  __device__ static raw from_f32(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+  __device__ static float to_f32(raw r) { return (float)__builtin_bit_cast(_Float16, r); }
+  __device__ static void unpack8(const uint4& v, float* o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
+      o[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+    }
+  }
+};
+
+struct F32 {
+  using raw = float;
+  static constexpr int SZ = 4;
+  static constexpr int KPL = 1;
+  __device__ static raw from_f32(float f) { return f; }
+  __device__ static float to_f32(raw r) { return r; }
+  __device__ static void unpack4(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x);
+    o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z);
+    o[3] = __uint_as_float(v.w);
+  }
+};
+
+// Elements held in one 16-byte word, and the unpack of such a word to fp32.
+template <class T> struct Vec;
+template <> struct Vec<BF16> {
+  static constexpr int N = 8;
+  __device__ static void unpack(const uint4& v, float* o) { BF16::unpack8(v, o); }
+};
+template <> struct Vec<F16> {
+  static constexpr int N = 8;
+  __device__ static void unpack(const uint4& v, float* o) { F16::unpack8(v, o); }
+};
+template <> struct Vec<F32> {
+  static constexpr int N = 4;
+  __device__ static void unpack(const uint4& v, float* o) { F32::unpack4(v, o); }
+};
+
+// One 32x32 MFMA step.  `a` / `b` are the lane's row fragments as 16-byte
+// words; step s consumes KPL elements starting at element s*KPL.  Callers
+// invoke it from fully unrolled loops so `s` is a compile-time constant.
+template <class T> struct Mfma;
+template <> struct Mfma<BF16> {
+  __device__ __forceinline__ static f32x16 step(const uint4* a, const uint4* b, int s, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                   __builtin_bit_cast(bf16x8, b[s]), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<F16> {
+  __device__ __forceinline__ static f32x16 step(const uint4* a, const uint4* b, int s, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[s]),
+                                                  __builtin_bit_cast(f16x8, b[s]), c, 0, 0, 0);
+  }
+};
+__device__ __forceinline__ float word(const uint4& v, int c) {
+  return __uint_as_float(c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w);
+}
+template <> struct Mfma<F32> {
+  __device__ __forceinline__ static f32x16 step(const uint4* a, const uint4* b, int s, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(word(a[s >> 2], s & 3), word(b[s >> 2], s & 3), c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Wave / block helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Exclusive prefix sum over a 256-thread block (4 waves).  `tmp` must hold 4
+// words.  Returns the exclusive prefix of `v`; *total receives the block sum.
+__device__ __forceinline__ uint32_t block_exclusive_scan_256(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  const int lane = lane_id();
+  const int w = threadIdx.x >> 6;
+  uint32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  if (lane == kWave - 1) tmp[w] = inc;
+  __syncthreads();
+  uint32_t wpre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t t = tmp[i];
+    if (i < w) wpre += t;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return wpre + inc - v;
+}
+
+}  // namespace fkm

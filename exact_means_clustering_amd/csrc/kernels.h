@@ -1,0 +1,89 @@
+// Host-side launchers for the k-means kernels (internal; the public ABI is
+// include/flashkm.h).  Every launcher enqueues on `s` and returns the
+// hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fkm {
+
+enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+// ---- assignment stage ------------------------------------------------------
+// Points per workgroup of the assign kernel for a given point-block count.
+constexpr int kAssignWaves = 4;
+inline int assign_rows_per_wg(int pb) { return kAssignWaves * 32 * pb; }
+// Point blocks (32 points each) per wave chosen for a shape.
+int assign_pick_pb(int dt, int D, int64_t N, int B);
+// Largest number of assign workgroups per instance over every pick.
+inline int64_t assign_max_wgs(int64_t N) { return (N + 127) / 128; }
+
+// Chat[r] = RNE(C[r] -> dtype), hb[r] = -0.5 * ||Chat[r]||^2 for r < rows.
+hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t rows, hipStream_t s);
+
+// Fused distance + running argmin.  part[b * nwg + wg] receives each
+// workgroup's fp64 sum of min_d2 (nwg = ceil(N / rows_per_wg(pb))).
+hipError_t launch_assign(int dt, int D, int pb, const void* X, const void* Chat, const float* hb, int64_t N,
+                         int K, int B, int32_t* labels, float* min_d2, double* part, hipStream_t s);
+
+// inertia[b] = sum_w part[b * nwg + w] in a fixed order (added to the old
+// value when `accumulate`); also copied to hist[b] if non-null.
+hipError_t launch_inertia_reduce(const double* part, int nwg, int B, double* inertia, double* hist,
+                                 bool accumulate, hipStream_t s);
+
+// ---- inverse mapping (stable LSD radix argsort + segment offsets) -----------
+constexpr int kSortTile = 4096;  // keys per sort workgroup
+inline int64_t sort_blocks(int64_t n) { return (n + kSortTile - 1) / kSortTile; }
+
+struct SortBuffers {
+  uint32_t* keys[2];
+  uint32_t* vals[2];
+  uint32_t* hist;   // [256 * nblk]
+  uint32_t* dtot;   // [256]
+};
+// Sorts rows by key = b*K + clamp(labels[b*N+i], 0, K-1) (stable).  On return
+// *sorted_keys / *perm point at the buffers holding the result.
+hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K, SortBuffers& buf,
+                                 const uint32_t** sorted_keys, const uint32_t** perm, hipStream_t s);
+// off[k] = #{rows with key < k} for k in [0, nseg]
+hipError_t launch_segment_offsets(const uint32_t* sorted_keys, int64_t n, uint32_t nseg, int32_t* off,
+                                  hipStream_t s);
+
+// ---- segment-local reductions ----------------------------------------------
+constexpr int kSegRows = 256;    // rows of the sorted order per wave chunk (level 1)
+constexpr int kSegGroup = 32;    // level-1 chunks per level-2 group
+inline int64_t seg_chunks(int64_t n) { return (n + kSegRows - 1) / kSegRows; }
+inline int64_t seg_groups(int64_t n) { return (seg_chunks(n) + kSegGroup - 1) / kSegGroup; }
+
+struct SegBuffers {
+  float* frag;     // [nchunks * 2 * D] fp32
+  double* gfrag;   // [ngroups * 2 * D] fp64
+};
+// Where each finished segment goes.  Means mode (S_acc == nullptr):
+// C_new[k] = segment sum / count, counts[k] = count, and an empty segment
+// copies C_prev[k] with count 0.  Accumulate mode (S_acc != nullptr):
+// S_acc[k] += segment sum (fp64) and n_acc[k] += count; empty segments are
+// left alone.  Every segment is finished by exactly one wave, so neither
+// mode needs atomics.
+struct SegOut {
+  const float* C_prev;
+  float* C_new;
+  int32_t* counts;
+  double* S_acc;
+  int64_t* n_acc;
+};
+hipError_t launch_segment_reduce(int dt, int D, const void* X, const uint32_t* perm, const uint32_t* sorted_keys,
+                                 const int32_t* off, int64_t n, uint32_t nseg, const SegOut& out,
+                                 SegBuffers& buf, hipStream_t s);
+
+// ---- streamed path helpers ---------------------------------------------------
+// C_new[k] = S[k] / n[k] (fp64 divide, rounded once to fp32) when n[k] > 0,
+// else C_prev[k]; counts are not produced.
+hipError_t launch_mean_from_sums(const double* S, const int64_t* n, int D, int64_t K, const float* C_prev,
+                                 float* C_new, hipStream_t s);
+hipError_t launch_zero_bytes(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace fkm

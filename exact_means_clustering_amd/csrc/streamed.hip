@@ -1,0 +1,168 @@
+// Out-of-core Lloyd iteration: chunked-stream overlap (Flash-KMeans paper page,
+// abstract; article section "Flash-KMeans が変える点", third point: when the
+// points do not fit in device memory, the host-to-device transfer of the
+// next chunk overlaps the computation on the current one).
+//
+// Two device slots hold point chunks.  A copy stream moves chunk c+1 into
+// its slot while the compute stream assigns chunk c, sorts its labels and
+// adds its per-cluster sums into fp64 accumulators (chunk order fixed, so the
+// result is deterministic).  Labels of each chunk go back to the host on the
+// copy stream.  After the last chunk of an iteration the means are formed
+// once from the fp64 sums.
+#include "kernels.h"
+#include "workspace.h"
+
+#include "../../include/flashkm.h"
+
+using namespace fkm;
+
+namespace {
+
+struct Res {
+  hipStream_t cs = nullptr, xs = nullptr;
+  hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
+  void* dev[16] = {};
+  int ndev = 0;
+  void* alloc(size_t bytes) {
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes < 256 ? 256 : bytes) != hipSuccess) return nullptr;
+    dev[ndev++] = p;
+    return p;
+  }
+  ~Res() {
+    if (cs) (void)hipStreamSynchronize(cs);
+    if (xs) (void)hipStreamSynchronize(xs);
+    for (int i = 0; i < ndev; ++i) (void)hipFree(dev[i]);
+    for (int i = 0; i < 2; ++i) {
+      if (copied[i]) (void)hipEventDestroy(copied[i]);
+      if (done[i]) (void)hipEventDestroy(done[i]);
+      if (freed[i]) (void)hipEventDestroy(freed[i]);
+    }
+    if (cs) (void)hipStreamDestroy(cs);
+    if (xs) (void)hipStreamDestroy(xs);
+  }
+};
+
+int bad(int code, const char* msg) { return fail(code, "%s", msg); }
+
+}  // namespace
+
+#define KS_HIP(expr, what)                                                             \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) {                                                            \
+      char m_[256];                                                                    \
+      snprintf(m_, sizeof(m_), "%s: %s", what, hipGetErrorString(e_));                 \
+      return bad(KM_EHIP, m_);                                           \
+    }                                                                                  \
+  } while (0)
+
+extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N, int32_t D, const float* C0,
+                                   int32_t K, int32_t iters, size_t device_x_budget, int32_t* labels_host,
+                                   float* C_out, double* inertia_host, double* inertia_hist_host, void* stream) {
+  err_buf()[0] = 0;
+  if (dtype != KM_F32 && dtype != KM_F16 && dtype != KM_BF16) return bad(KM_EUNSUPPORTED, "unsupported dtype");
+  if (!(D == 16 || D == 32 || D == 64 || D == 128 || D == 256))
+    return bad(KM_EUNSUPPORTED, "unsupported D (supported: 16, 32, 64, 128, 256)");
+  if (K < 1 || N < K) return bad(KM_EINVAL, "need 1 <= K <= N");
+  if (iters < 1) return bad(KM_EINVAL, "iters must be >= 1");
+  if (!X_host || !C0 || !labels_host || !C_out || !inertia_host)
+    return bad(KM_EINVAL, "X_host, C0, labels_host, C_out and inertia_host must be non-null");
+  if (((uintptr_t)X_host & 15) != 0) return bad(KM_EINVAL, "X_host must be 16-byte aligned");
+  {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, X_host) != hipSuccess || attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      return bad(KM_EINVAL, "X_host must be page-locked host memory (hipHostMalloc / pinned tensor)");
+    }
+  }
+  const int sz = dtype_size(dtype);
+  const size_t row_bytes = (size_t)D * sz;
+  int64_t chunk = (int64_t)(device_x_budget / 2 / row_bytes);
+  if (chunk > ((int64_t)1 << 30)) chunk = (int64_t)1 << 30;
+  if (chunk < 1) return bad(KM_EINVAL, "device_x_budget is smaller than two rows");
+  if (chunk > N) chunk = N;
+  const int64_t nch = (N + chunk - 1) / chunk;
+
+  Res r;
+  KS_HIP(hipStreamSynchronize((hipStream_t)stream), "caller stream sync");
+  KS_HIP(hipStreamCreateWithFlags(&r.cs, hipStreamNonBlocking), "stream create");
+  KS_HIP(hipStreamCreateWithFlags(&r.xs, hipStreamNonBlocking), "stream create");
+  for (int i = 0; i < 2; ++i) {
+    KS_HIP(hipEventCreateWithFlags(&r.copied[i], hipEventDisableTiming), "event create");
+    KS_HIP(hipEventCreateWithFlags(&r.done[i], hipEventDisableTiming), "event create");
+    KS_HIP(hipEventCreateWithFlags(&r.freed[i], hipEventDisableTiming), "event create");
+  }
+
+  // device buffers
+  void* xslot[2];
+  int32_t* lslot[2];
+  for (int i = 0; i < 2; ++i) {
+    xslot[i] = r.alloc(al256((size_t)chunk * row_bytes));
+    lslot[i] = (int32_t*)r.alloc(al256((size_t)chunk * 4));
+    if (!xslot[i] || !lslot[i]) return bad(KM_ENOMEM, "device slot allocation failed");
+  }
+  const size_t ws_bytes = make_layout(chunk > K ? chunk : K, D, K, 1, dtype).total;
+  void* ws = r.alloc(ws_bytes);
+  double* S_acc = (double*)r.alloc((size_t)K * D * 8);
+  int64_t* n_acc = (int64_t*)r.alloc((size_t)K * 8);
+  double* J_dev = (double*)r.alloc((size_t)iters * 8);
+  if (!ws || !S_acc || !n_acc || !J_dev) return bad(KM_ENOMEM, "device workspace allocation failed");
+
+  const int64_t wsN = chunk > K ? chunk : K;
+  Work w = carve(ws, make_layout(wsN, D, K, 1, dtype));
+
+  const char* xh = (const char*)X_host;
+  // both slots start free
+  for (int i = 0; i < 2; ++i) KS_HIP(hipEventRecord(r.freed[i], r.xs), "event record");
+
+  for (int t = 0; t < iters; ++t) {
+    const float* Cs = t == 0 ? C0 : C_out;
+    KS_HIP(launch_prep(dtype, D, Cs, w.chat, w.hb, K, r.cs), "centroid prep launch");
+    KS_HIP(launch_zero_bytes(S_acc, (size_t)K * D * 8, r.cs), "zero launch");
+    KS_HIP(launch_zero_bytes(n_acc, (size_t)K * 8, r.cs), "zero launch");
+    KS_HIP(launch_zero_bytes(J_dev + t, 8, r.cs), "zero launch");
+
+    auto h2d = [&](int64_t c) -> int {
+      const int sl = (int)(c & 1);
+      const int64_t rows = (c + 1) * chunk <= N ? chunk : N - c * chunk;
+      KS_HIP(hipStreamWaitEvent(r.xs, r.freed[sl], 0), "stream wait");
+      KS_HIP(hipMemcpyAsync(xslot[sl], xh + (size_t)c * chunk * row_bytes, (size_t)rows * row_bytes,
+                            hipMemcpyHostToDevice, r.xs),
+             "H2D copy");
+      KS_HIP(hipEventRecord(r.copied[sl], r.xs), "event record");
+      return KM_OK;
+    };
+    if (int rc = h2d(0)) return rc;
+    for (int64_t c = 0; c < nch; ++c) {
+      const int sl = (int)(c & 1);
+      const int64_t rows = (c + 1) * chunk <= N ? chunk : N - c * chunk;
+      if (c + 1 < nch)
+        if (int rc = h2d(c + 1)) return rc;
+      KS_HIP(hipStreamWaitEvent(r.cs, r.copied[sl], 0), "stream wait");
+      const int pb = assign_pick_pb(dtype, D, rows, 1);
+      KS_HIP(launch_assign(dtype, D, pb, xslot[sl], w.chat, w.hb, rows, K, 1, lslot[sl], nullptr, w.part, r.cs),
+             "assign launch");
+      const int64_t nwg = (rows + assign_rows_per_wg(pb) - 1) / assign_rows_per_wg(pb);
+      KS_HIP(launch_inertia_reduce(w.part, (int)nwg, 1, J_dev + t, nullptr, true, r.cs), "inertia launch");
+      const uint32_t* skeys = nullptr;
+      const uint32_t* perm = nullptr;
+      KS_HIP(launch_argsort_labels(lslot[sl], rows, 1, K, w.sort, &skeys, &perm, r.cs), "argsort launch");
+      KS_HIP(launch_segment_offsets(skeys, rows, (uint32_t)K, w.off, r.cs), "segment offsets launch");
+      SegOut so{nullptr, nullptr, nullptr, S_acc, n_acc};
+      KS_HIP(launch_segment_reduce(dtype, D, xslot[sl], perm, skeys, w.off, rows, (uint32_t)K, so, w.seg, r.cs),
+             "segment reduce launch");
+      KS_HIP(hipEventRecord(r.done[sl], r.cs), "event record");
+      KS_HIP(hipStreamWaitEvent(r.xs, r.done[sl], 0), "stream wait");
+      KS_HIP(hipMemcpyAsync(labels_host + c * chunk, lslot[sl], (size_t)rows * 4, hipMemcpyDeviceToHost, r.xs),
+             "labels D2H copy");
+      KS_HIP(hipEventRecord(r.freed[sl], r.xs), "event record");
+    }
+    KS_HIP(launch_mean_from_sums(S_acc, n_acc, D, K, Cs, C_out, r.cs), "mean launch");
+  }
+  KS_HIP(hipStreamSynchronize(r.cs), "compute stream sync");
+  KS_HIP(hipStreamSynchronize(r.xs), "copy stream sync");
+  KS_HIP(hipMemcpy(inertia_host, J_dev + (iters - 1), 8, hipMemcpyDeviceToHost), "inertia copy");
+  if (inertia_hist_host) KS_HIP(hipMemcpy(inertia_hist_host, J_dev, (size_t)iters * 8, hipMemcpyDeviceToHost), "inertia copy");
+  return KM_OK;
+}

@@ -1,0 +1,141 @@
+/*
+ * flashkm.h — C ABI of the MI355X (gfx950) exact Lloyd k-means library.
+ *
+ * The operations follow "Flash-KMeans: Fast and Memory-Efficient Exact
+ * K-Means" (paper page, abstract) and the article "Hacker Newsが捉えた
+ * Flash-KMeans、Exact K-MeansをGPUのonline primitiveへ" (section
+ * "Flash-KMeans が変える点"):
+ *   - an assignment stage that fuses the point-to-centroid distance
+ *     computation with a running argmin, so no N x K distance matrix is ever
+ *     written to memory (FlashAssign);
+ *   - a centroid update stage that first builds the cluster-sorted inverse
+ *     mapping of the labels and then reduces each cluster's contiguous
+ *     segment of points, with no global atomics (sort-inverse update);
+ *   - chunked streaming of a host-resident point set that overlaps the
+ *     host-to-device copies with compute (chunked-stream overlap).
+ * The iteration itself is the unchanged, exact Lloyd iteration.
+ *
+ * Conventions shared by every entry point
+ *   Shapes: X is [B, N, D] row-major (B independent instances of N points;
+ *     B = 1 is the plain unbatched problem).  Centroids are [B, K, D] fp32
+ *     row-major.  Labels are [B, N] int32 with values in [0, K) local to the
+ *     instance.  Counts are [B, K] int32.  Inertia is [B] fp64.
+ *   dtype (km_dtype) is the storage type of X.  Assignment uses the
+ *     centroids rounded to nearest-even into that type (the fp32 centroid
+ *     state itself is never rounded); squared centroid norms come from the
+ *     rounded values; accumulation is fp32.  Ties go to the lowest index.
+ *   Supported D: 16, 32, 64, 128, 256.  1 <= K <= N, B >= 1, B*N < 2^31.
+ *   In-core pointers are DEVICE pointers (hipMalloc / torch CUDA tensors),
+ *     contiguous; X must be 16-byte aligned, everything else naturally
+ *     aligned.  The caller owns every buffer.  The in-core entry points never
+ *     allocate or free memory: scratch space comes from the caller's
+ *     workspace `ws` of at least kmeans_workspace_bytes(...) bytes.
+ *   stream is a hipStream_t passed as void* (NULL = the null stream).
+ *     In-core calls only enqueue work on it; results are valid once the
+ *     stream has been synchronised.  Calls that share a workspace must be
+ *     ordered on one stream.
+ *   Errors: arguments are validated before anything is enqueued; on any
+ *     failure the call returns a non-zero km_status, enqueues nothing (for
+ *     validation errors) and kmeans_last_error() describes it.  HIP launch
+ *     or API failures return KM_EHIP.  Device-side faults surface at the
+ *     caller's next synchronisation.  No C++ exception crosses the ABI and
+ *     the library prints nothing.  Non-finite inputs give unspecified labels
+ *     and centroids (memory safety is kept).
+ *   Determinism: identical inputs on the same device give bitwise identical
+ *     outputs; no result depends on atomics or scheduling order.
+ */
+#ifndef FLASHKM_H
+#define FLASHKM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define KM_API __attribute__((visibility("default")))
+#else
+#define KM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KM_F32 = 0, KM_F16 = 1, KM_BF16 = 2 } km_dtype;
+
+typedef enum {
+  KM_OK = 0,
+  KM_EINVAL = 1,       /* bad argument (null pointer, K > N, iters < 1, ...) */
+  KM_EUNSUPPORTED = 2, /* unsupported D or dtype                            */
+  KM_EWORKSPACE = 3,   /* workspace smaller than kmeans_workspace_bytes()   */
+  KM_EHIP = 4,         /* a HIP runtime call or kernel launch failed        */
+  KM_ENOMEM = 5        /* kmeans_fit_streamed could not allocate its slots  */
+} km_status;
+
+/* Bytes of device workspace the in-core entry points need for this shape.
+ * Returns 0 for an invalid or unsupported shape.  The same workspace serves
+ * kmeans_assign, kmeans_update and kmeans_fit. */
+KM_API size_t kmeans_workspace_bytes(int64_t N, int32_t D, int32_t K, int32_t B, int32_t dtype);
+
+/* Assignment stage (FlashAssign; paper page abstract, "assignment stage";
+ * article section "Flash-KMeans が変える点", first point).
+ *   labels[b,i]  = argmin_k || x_bi - round(C_bk) ||^2   (lowest k on ties)
+ *   min_d2[b,i]  = that minimum squared distance (fp32)   [nullable]
+ *   inertia[b]   = sum_i min_d2[b,i], accumulated in fp64 [nullable]
+ * X [B,N,D] dtype; C [B,K,D] fp32; labels [B,N] int32 (required). */
+KM_API int kmeans_assign(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
+                  const float* C, int32_t K,
+                  int32_t* labels, float* min_d2, double* inertia,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Centroid update stage (sort-inverse update; paper page abstract, "centroid
+ * update stage"; article section "Flash-KMeans が変える点", second point).
+ *   counts[b,k] = #{i : labels[b,i] = k}
+ *   C_new[b,k]  = (1/counts) * sum_{i: labels[b,i]=k} x_bi     if counts > 0
+ *               = C_prev[b,k]                                 otherwise
+ * Sums are fp32 within fixed chunks of the cluster-sorted order and fp64
+ * across chunks; the division is IEEE fp32.  C_new may alias C_prev.
+ * Labels outside [0,K) are a caller error: results are unspecified but every
+ * memory access stays in bounds. */
+KM_API int kmeans_update(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
+                  const int32_t* labels, int32_t K,
+                  const float* C_prev, float* C_new, int32_t* counts,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* The exact Lloyd iteration (paper page abstract; article section 論文の要点):
+ * exactly `iters` rounds of assign-then-update starting from C0.
+ * Returns labels and inertia of the LAST assignment, and C_out = the
+ * centroids after the LAST update.  inertia [B] fp64 device (required);
+ * inertia_hist [iters, B] fp64 device (nullable) receives every round's
+ * inertia.  C_out may alias C0.  Resuming is fit(X, C_t, iters - t). */
+KM_API int kmeans_fit(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
+               const float* C0, int32_t K, int32_t iters,
+               int32_t* labels, float* C_out, double* inertia, double* inertia_hist,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* Out-of-core Lloyd iteration (chunked-stream overlap; paper page abstract;
+ * article section "Flash-KMeans が変える点", third point).  B = 1.
+ *   X_host         [N,D] dtype in PAGE-LOCKED host memory (hipHostMalloc or
+ *                  a pinned torch tensor); it never has to fit on the device.
+ *   C0, C_out      [K,D] fp32 DEVICE pointers (may alias).
+ *   labels_host    [N] int32 host memory (pinned recommended).
+ *   inertia_host   [1] fp64 host; inertia_hist_host [iters] fp64 host or NULL.
+ *   device_x_budget  bytes of device memory the point chunks may occupy
+ *                  (two slots of half the budget each).
+ * Same results as kmeans_fit for labels and inertia of a given centroid
+ * state; centroid sums are combined chunk by chunk in fp64 (in chunk order),
+ * so centroids agree with the in-core path to rounding.  Synchronous: all
+ * outputs are final on return.  This entry point allocates (and frees) its
+ * own device slots and workspace; KM_ENOMEM if that fails. */
+KM_API int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N, int32_t D,
+                        const float* C0, int32_t K, int32_t iters, size_t device_x_budget,
+                        int32_t* labels_host, float* C_out, double* inertia_host,
+                        double* inertia_hist_host, void* stream);
+
+/* Text of the last error set on the calling thread ("" if none). */
+KM_API const char* kmeans_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHKM_H */

@@ -1,0 +1,226 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Sizes span several assign tiles (64 centroids, 128-512 points), several sort
+tiles (4096 keys) and update chunks (256 sorted rows per chunk, 32 chunks per
+group) with ragged tails.  Full-size workloads check sampled rows plus
+properties that hold at any size.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def km():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_means_clustering_amd as km
+    return km
+
+
+def _stats_ok(stats):
+    assert all(s["centroid_err"] <= H.TOL_CENTROID for s in stats)
+
+
+def test_c1_full(km):
+    p = datagen.make("c1")
+    _stats_ok(H.teacher_forced(km, p.X, p.C0, p.iters, tag="c1"))
+
+
+def test_c2_scaled_ragged(km):
+    p = datagen.make("c2", n=70001, k=300, seed=1)
+    _stats_ok(H.teacher_forced(km, p.X, p.C0, 4, tag="c2s"))
+
+
+def test_c3_scaled_zipf(km):
+    p = datagen.make("c3", n=65539, k=2053, seed=2)
+    _stats_ok(H.teacher_forced(km, p.X, p.C0, 3, tag="c3s"))
+
+
+def test_c4_scaled_batched(km):
+    p = datagen.make("c4", n=3001, k=77, batch=5, seed=3)
+    _stats_ok(H.teacher_forced(km, p.X, p.C0, 3, tag="c4s"))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("d", [16, 64, 256])
+def test_dims_and_dtypes(km, dtype, d):
+    X, C0, _, _ = datagen.mixture(5003, d, 40, dtype=dtype, center_dist="normal", center_scale=2.0, sigma=1.0,
+                                  weights=None, workload_code=50, seed=d, k=45)
+    _stats_ok(H.teacher_forced(km, X, C0, 2, tag=f"{dtype}-D{d}"))
+
+
+def test_tiny_ragged(km):
+    X, C0, _, _ = datagen.mixture(37, 32, 4, dtype="bf16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                  weights=None, workload_code=51, seed=0, k=5)
+    _stats_ok(H.teacher_forced(km, X, C0, 3, tag="tiny"))
+
+
+def test_k_equals_one(km):
+    X, C0, _, _ = datagen.mixture(9000, 128, 3, dtype="fp16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                  weights=None, workload_code=52, seed=0, k=1)
+    _stats_ok(H.teacher_forced(km, X, C0, 2, tag="k1"))
+    labels, C, J, _ = km.fit(X.cuda(), C0.cuda(), 2)
+    assert int(labels.max()) == 0
+    mean = X[0].double().mean(0)
+    assert torch.allclose(C[0, 0].cpu().double(), mean, rtol=1e-4, atol=1e-5)
+
+
+def test_k_equals_n_identity(km):
+    X, _, _, _ = datagen.mixture(700, 64, 700, dtype="bf16", center_dist="normal", center_scale=3.0, sigma=1.0,
+                                 weights=None, workload_code=53, seed=0)
+    Xu = torch.unique(X[0].float(), dim=0)
+    Xu = Xu[torch.randperm(Xu.shape[0], generator=torch.Generator().manual_seed(0))]
+    Xb = Xu.to(torch.bfloat16)[None].contiguous()
+    C0 = Xb.float()
+    labels, md, J = km.assign(Xb.cuda(), C0.cuda(), want_min_d2=True)
+    assert torch.equal(labels.cpu()[0], torch.arange(Xb.shape[1], dtype=torch.int32))
+    assert float(J[0]) == 0.0 and float(md.abs().max()) == 0.0
+    Cn, cnt = km.update(Xb.cuda(), labels, C0.cuda())
+    assert torch.equal(Cn.cpu(), C0) and int(cnt.min()) == 1
+
+
+def test_duplicate_centroids_lowest_index(km):
+    X, C0, _, _ = datagen.mixture(20000, 128, 30, dtype="fp16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                  weights=None, workload_code=54, seed=0, k=40)
+    C0 = C0.clone()
+    C0[0, 33] = C0[0, 7]       # exact duplicates: index 33 must never win
+    C0[0, 39] = C0[0, 2]
+    labels, _, _ = km.assign(X.cuda(), C0.cuda())
+    lab = labels.cpu()
+    assert not bool((lab == 33).any()) and not bool((lab == 39).any())
+    assert bool((lab == 7).any()) and bool((lab == 2).any())
+    _stats_ok(H.teacher_forced(km, X, C0, 2, tag="dup"))
+
+
+def test_identical_rows(km):
+    X = torch.full((1, 5000, 32), 0.75, dtype=torch.bfloat16)
+    X[0, :, 3] = -1.5
+    C0 = torch.zeros(1, 6, 32)
+    C0[0, :] = X[0, 0].float()
+    labels, C, J, _ = km.fit(X.cuda(), C0.cuda(), 2)
+    assert int(labels.abs().max()) == 0 and float(J[0]) == 0.0
+    assert torch.equal(C.cpu(), C0)
+
+
+def test_forced_empty_clusters(km):
+    X, C0, _, _ = datagen.mixture(30000, 64, 20, dtype="bf16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                  weights=None, workload_code=55, seed=0, k=24)
+    C0 = C0.clone()
+    C0[0, 5] = 1e4             # far away: empty for every iteration
+    C0[0, 17] = -1e4
+    stats = H.teacher_forced(km, X, C0, 3, tag="empty")
+    _stats_ok(stats)
+    _, C, _, _ = km.fit(X.cuda(), C0.cuda(), 3)
+    assert torch.equal(C.cpu()[0, 5], C0[0, 5]) and torch.equal(C.cpu()[0, 17], C0[0, 17])
+
+
+@pytest.mark.parametrize("case", ["zipf", "one_cluster", "two_clusters"])
+def test_update_long_segments(km, case):
+    """Skewed labels: one segment spans many chunks and groups (the hot-cluster
+    contention case of the update)."""
+    n, k = 600_001, 1000
+    X, _, _, _ = datagen.mixture(n, 128, 8, dtype="bf16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                 weights=None, workload_code=56, seed=0)
+    if case == "zipf":
+        lab = datagen.zipf_labels(n, k, 1.1, seed=1)
+    elif case == "one_cluster":
+        lab = np.full((1, n), 731, dtype=np.int32)
+    else:
+        lab = np.where(np.arange(n) % 3 == 0, 5, 998).astype(np.int32)[None]
+    C_prev = torch.randn(1, k, 128, generator=torch.Generator().manual_seed(0))
+    labels = torch.from_numpy(lab).cuda()
+    C_new, counts = km.update(X.cuda(), labels, C_prev.cuda())
+    torch.cuda.synchronize()
+    Xd = H.decode(X[0], "bf16")
+    err = H.check_update(Xd, lab[0], C_prev[0].numpy(), C_new.cpu()[0].numpy(), counts.cpu()[0].numpy(), k,
+                         tag=case)
+    H.log(f"update {case}: centroid err {err:.2e}, max count {int(counts.max())}")
+
+
+def test_batched_equals_unbatched(km):
+    p = datagen.make("c4", n=4096, k=64, batch=3, seed=4)
+    lb, Cb, Jb, _ = km.fit(p.X.cuda(), p.C0.cuda(), 3)
+    for b in range(3):
+        l1, C1, J1, _ = km.fit(p.X[b:b + 1].contiguous().cuda(), p.C0[b:b + 1].contiguous().cuda(), 3)
+        assert torch.equal(l1[0], lb[b]) and torch.equal(C1[0], Cb[b]) and torch.equal(J1[0], Jb[b])
+    # 2-D inputs are the B = 1 case
+    l2, C2, J2, _ = km.fit(p.X[0].contiguous().cuda(), p.C0[0].contiguous().cuda(), 3)
+    assert torch.equal(l2, lb[0]) and torch.equal(C2, Cb[0])
+
+
+def test_determinism_and_resume(km):
+    p = datagen.make("c3", n=50000, k=777, seed=6)
+    X, C0 = p.X.cuda(), p.C0.cuda()
+    a = km.fit(X, C0, 4, history=True)
+    b = km.fit(X, C0, 4, history=True)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    # resume: 4 iterations == 1 iteration, then 3 more from its centroids
+    _, C1, _, _ = km.fit(X, C0, 1)
+    c = km.fit(X, C1, 3, history=True)
+    assert torch.equal(c[0], a[0]) and torch.equal(c[1], a[1]) and torch.equal(c[3], a[3][1:])
+
+
+def test_no_nk_buffer(km):
+    """The assignment never holds an N x K buffer: peak device memory during a
+    call stays at inputs + outputs + the declared workspace."""
+    n, k, d = 1 << 18, 4096, 128
+    X = torch.randn(n, d, device="cuda").to(torch.bfloat16)
+    C = torch.randn(k, d, device="cuda")
+    ws = torch.empty(km.workspace_bytes(n, d, k, 1, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    km.assign(X, C, ws=ws)
+    torch.cuda.synchronize()
+    extra = torch.cuda.max_memory_allocated() - base
+    assert extra < n * 16 + (1 << 20), extra          # labels + inertia only
+    assert ws.numel() < n * k // 16                   # workspace is O(N + K), not O(N*K)
+
+
+def test_streamed_matches_in_core(km):
+    p = datagen.make("c5", n=300_000, k=128, seed=7)
+    X = p.X[0]
+    budget = 2 * 40_000 * 128 * 2                    # 40k-row slots: 8 chunks
+    Xp = X.pin_memory()
+    lab_s, C_s, J_s, hist_s = km.fit_streamed(Xp, p.C0[0].cuda(), 3, budget, history=True)
+    lab_i, C_i, J_i, hist_i = km.fit(X.cuda(), p.C0[0].cuda(), 3, history=True)
+    torch.cuda.synchronize()
+    # same kernels per row: labels of the first iteration agree exactly; the
+    # later ones may differ only through centroid rounding at the 1e-7 level
+    assert abs(hist_s[0] - float(hist_i[0, 0])) <= 1e-9 * hist_s[0]
+    assert abs(J_s - float(J_i[0])) <= 1e-5 * J_s
+    Xd = H.decode(X, "fp16")
+    rms = float(np.sqrt(np.einsum("ij,ij->i", Xd, Xd).mean()))
+    import oracle
+    assert oracle.centroid_rel_err(C_s.cpu().numpy(), C_i.cpu().numpy(), rms) <= 1e-4
+    mism = int((lab_s != lab_i.cpu()).sum())
+    assert mism <= 1e-4 * X.shape[0], mism
+    # teacher-forced: the streamed update from its own labels matches the oracle
+    _, C_prev, _, _ = km.fit_streamed(Xp, p.C0[0].cuda(), 2, budget)
+    H.check_assign(Xd, C_prev.cpu().numpy(), lab_s.numpy(), J_s, "fp16", tag="streamed")
+
+
+@pytest.mark.slow
+def test_c4_full(km):
+    p = datagen.make("c4")
+    _stats_ok(H.teacher_forced(km, p.X, p.C0, 2, tag="c4", check_fit=False))
+
+
+@pytest.mark.slow
+def test_c2_full_sampled(km):
+    p = datagen.make("c2")
+    _stats_ok(H.teacher_forced(km, p.X, p.C0, 2, sample=16384, tag="c2", check_fit=False))
+
+
+@pytest.mark.slow
+def test_c3_full_sampled(km):
+    p = datagen.make("c3")
+    _stats_ok(H.teacher_forced(km, p.X, p.C0, 1, sample=2048, tag="c3", check_fit=False))
