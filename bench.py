@@ -1,0 +1,211 @@
+"""Throughput of one exact Lloyd iteration (assign + sort-inverse update) on one MI355X.
+
+Default workload (--config c3): N=8,388,608 points, D=128, bf16 storage,
+K=65,536 centroids, 65,536-component Gaussian mixture with Zipf(1.1)
+weights (synthetic, seeded; the pages name no dataset).
+
+A step is one full Lloyd iteration through the C ABI on inputs already
+resident in HBM: kmeans_assign (centroid prep + fused MFMA distance/argmin +
+inertia) then kmeans_update (radix argsort + offsets + segment means).  HIP
+events on the stream the library launches on time each call.  Prints one
+JSON line.  `--config` picks another workload (c1, c2, c4, c5).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Lloyd iter/s + assign TFLOP/s (2NKD) at N=8M,D=128,K=64K; % of roofline"
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--n", type=int, default=None, help="override rows (tests / quick runs)")
+    ap.add_argument("--k", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=None, help="rows in the oracle timing sample")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="JSON file with measured HBM bytes per assign launch (from rocprofv3 counters)")
+    return ap.parse_args()
+
+
+def cpu_baseline(p, sample_rows):
+    """Time the fp64 oracle (as it stands) for one Lloyd iteration on a row
+    sample of the same workload, scaled linearly to the full N."""
+    import oracle
+    from tests.gpu_harness import decode
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = int(blas[0]["num_threads"]) if blas else 1
+    except Exception:  # pragma: no cover
+        cores = 1
+    B = p.B
+    rows = min(sample_rows, p.N)
+    Xs = p.X[0, :rows]
+    Xd = decode(Xs, p.dtype)
+    C = p.C0[0].numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    Ch = oracle.round_to_format(C, p.dtype)
+    lab, dmin = oracle.assign(Xd, Ch)
+    oracle.inertia(dmin)
+    oracle.update(Xd, lab, C, p.K)
+    dt = time.perf_counter() - t0
+    sec_per_iter = dt * (p.N / rows) * B
+    return {"value": 1.0 / sec_per_iter, "unit": "iter/s", "cores": cores, "kind": "oracle",
+            "sample": (f"one oracle Lloyd iteration (fp64 assign + update) on the first {rows:,} of "
+                       f"{p.N:,} rows x {B} instance(s), all K={p.K:,} centroids, {dt:.1f} s, scaled "
+                       f"linearly by N/{rows:,}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+
+    import datagen
+    import exact_means_clustering_amd as km
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(2)
+    name = args.config
+    if name == "c5":
+        return bench_streamed(args)
+    t0 = time.time()
+    p = datagen.make(name, n=args.n, k=args.k)
+    print(f"[bench] generated {name}: B={p.B} N={p.N} D={p.D} K={p.K} {p.dtype} in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    X = (p.X if p.B > 1 else p.X[0]).to(dev)
+    C0 = (p.C0 if p.B > 1 else p.C0[0]).to(dev)
+    B, N, D, K = p.B, p.N, p.D, p.K
+    dt_torch = X.dtype
+    ws = torch.empty(km.workspace_bytes(N, D, K, B, dt_torch), dtype=torch.uint8, device=dev)
+    labels = torch.empty(X.shape[:-1], dtype=torch.int32, device=dev)
+    C = C0.clone()
+    C_next = torch.empty_like(C)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        nonlocal C, C_next
+        if ev is not None:
+            ev[0].record(stream)
+        km.assign(X, C, ws=ws, labels=labels)
+        if ev is not None:
+            ev[1].record(stream)
+        km.update(X, labels, C, C_new=C_next, ws=ws)
+        if ev is not None:
+            ev[2].record(stream)
+        C, C_next = C_next, C
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    assign_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    update_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_step = total_ms / args.steps
+    a_ms = float(np.mean(assign_ms))
+    u_ms = float(np.mean(update_ms))
+    flops = 2.0 * B * N * K * D
+    a_tflops = flops / (a_ms * 1e-3) / 1e12
+    sz = X.element_size()
+    upd_bytes = B * (N * D * sz + 4 * N + 4 * K * D + 4 * K)
+    u_gbs = upd_bytes / (u_ms * 1e-3) / 1e9
+    peak = PEAK_TFLOPS[p.dtype]
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get(name)
+    out = {
+        "metric": METRIC,
+        "value": 1000.0 / ms_step,
+        "unit": "iter/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{name}: " + datagen.WORKLOADS[name]["desc"], "B": B, "N": N, "D": D, "K": K,
+                   "storage": p.dtype, "accumulate": "fp32", "step": "kmeans_assign + kmeans_update"},
+        "assign_ms": a_ms,
+        "update_ms": u_ms,
+        "assign_tflops": a_tflops,
+        "assign_frac_mfma_peak": a_tflops / peak,
+        "update_gbs": u_gbs,
+        "update_frac_hbm_peak": u_gbs / PEAK_HBM_GBS,
+        "roofline": {"bound": "mfma", "achieved": a_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": a_tflops / peak, "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or {"c1": 65536, "c2": 65536, "c3": 16384, "c4": 4096}[name]
+        out["cpu_baseline"] = cpu_baseline(p, sample)
+    print(json.dumps(out), flush=True)
+
+
+def bench_streamed(args):
+    """Out-of-core workload: X in pinned host memory, streamed in chunks."""
+    import torch
+
+    import datagen
+    import exact_means_clustering_amd as km
+
+    n = args.n or (1 << 27)
+    t0 = time.time()
+    p = datagen.make("c5", n=n, k=args.k)
+    X = p.X[0].pin_memory()
+    budget = X.numel() * X.element_size() // 8       # device slots hold 1/8 of X
+    print(f"[bench] generated c5 N={p.N} in {time.time() - t0:.1f}s, budget {budget / 2**30:.2f} GiB",
+          file=sys.stderr, flush=True)
+    C0 = p.C0[0].cuda()
+    km.fit_streamed(X, C0, 1, budget)                 # warm-up
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    iters = max(1, args.steps)
+    km.fit_streamed(X, C0, iters, budget)
+    dt = time.perf_counter() - t1
+    gb = X.numel() * X.element_size() / 1e9
+    out = {"metric": METRIC, "value": iters / dt, "unit": "iter/s", "n_gpus": 1, "steps": iters, "warmup": 1,
+           "ms_per_step": dt / iters * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": p.dtype, "data": "synthetic",
+           "config": {"workload": f"c5 (scaled to N={p.N:,}): pinned-host X streamed through two device slots",
+                      "N": p.N, "D": p.D, "K": p.K, "device_x_budget": budget},
+           "h2d_gbs": gb * iters / dt,
+           "assign_tflops_effective": 2.0 * p.N * p.K * p.D * iters / dt / 1e12}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -37,8 +37,8 @@ def lib_path() -> str:
     return os.path.join(_HERE, _LIB_NAME)
 
 
-def _load():
-    path = lib_path()
+def _load(path=None):
+    path = path or lib_path()
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built: run `python -m exact_means_clustering_amd.build` "
                           "(there is no CPU fallback)")

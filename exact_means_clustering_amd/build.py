@@ -37,8 +37,13 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Per-source extra flags.  The assign kernel's running max needs no NaN
+# canonicalisation (non-finite inputs give unspecified labels by contract).
+EXTRA = {"assign.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src, obj, verbose):
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

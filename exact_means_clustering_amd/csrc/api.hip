@@ -42,10 +42,10 @@ int check_ws(const void* ws, size_t ws_bytes, const Layout& L) {
 int run_assign(const void* X, int dt, int64_t N, int D, int B, const float* C, int K, int32_t* labels,
                float* min_d2, double* inertia, double* hist, Work& w, hipStream_t s) {
   KM_HIP(launch_prep(dt, D, C, w.chat, w.hb, (int64_t)B * K, s), "centroid prep launch");
-  const int pb = assign_pick_pb(dt, D, N, B);
-  KM_HIP(launch_assign(dt, D, pb, X, w.chat, w.hb, N, K, B, labels, min_d2, w.part, s), "assign launch");
+  const AssignConfig cfg = assign_pick(dt, D, N, B);
+  KM_HIP(launch_assign(dt, D, cfg, X, w.chat, w.hb, N, K, B, labels, min_d2, w.part, s), "assign launch");
   if (inertia) {
-    const int64_t nwg = (N + assign_rows_per_wg(pb) - 1) / assign_rows_per_wg(pb);
+    const int64_t nwg = (N + cfg.rows() - 1) / cfg.rows();
     KM_HIP(launch_inertia_reduce(w.part, (int)nwg, B, inertia, hist, false, s), "inertia launch");
   }
   return KM_OK;

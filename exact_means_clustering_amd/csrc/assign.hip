@@ -29,6 +29,8 @@
 #include "kernels.h"
 
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 namespace fkm {
 
@@ -60,17 +62,36 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, 
 // ---------------------------------------------------------------------------
 // fused assign
 // ---------------------------------------------------------------------------
-constexpr int kTileK = 64;  // centroids per LDS tile
-
-template <class T, int D, int PB>
+template <class T, int D, int PB, int W>
 struct AssignCfg {
   static constexpr int RB = D * T::SZ;                 // bytes per row
+#ifndef FKM_TK
+  static constexpr int TK = RB <= 256 ? 128 : 64;      // centroids per LDS tile
+#else
+  static constexpr int TK = RB <= 256 ? FKM_TK : 64;
+#endif
+#ifndef FKM_SBG
+  static constexpr int SBG = 1;                        // 32-centroid sub-blocks per MFMA group
+#else
+  static constexpr int SBG = FKM_SBG;
+#endif
+#ifndef FKM_DELAY
+  static constexpr bool DELAY = true;                  // reduce group j-1 behind group j's MFMAs
+#else
+  static constexpr bool DELAY = FKM_DELAY;
+#endif
+#ifndef FKM_APF
+  static constexpr bool APF = false;                   // prefetch the next group's A fragments
+#else
+  static constexpr bool APF = FKM_APF;
+#endif
   static constexpr int NCH = RB / 16;                  // 16-byte chunks per row
   static constexpr int HV = NCH / 2;                   // chunks per lane-half fragment
   static constexpr int STEPS = (D / 2) / T::KPL;       // MFMA steps per 32x32 tile
-  static constexpr int TILE_CH = kTileK * NCH;         // chunks per LDS tile
-  static constexpr int PRE = (TILE_CH + 255) / 256;    // chunks per thread per tile load
-  static constexpr int ROWS = kAssignWaves * 32 * PB;  // points per workgroup
+  static constexpr int TILE_CH = TK * NCH;             // chunks per LDS tile
+  static constexpr int THREADS = W * 64;
+  static constexpr int PRE = (TILE_CH + THREADS - 1) / THREADS;  // chunks per thread per tile load
+  static constexpr int ROWS = W * 32 * PB;                       // points per workgroup
   static_assert(NCH >= 2 && (NCH & (NCH - 1)) == 0, "row must be a power-of-two number of 16B chunks");
 };
 
@@ -83,12 +104,12 @@ __device__ __forceinline__ float max16(const f32x16& a) {
   return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, a[15]));
 }
 
-// Running (max, argmax) update for one lane and one 32-centroid tile.
-// `base` is the centroid index of accumulator register 0 for this lane.
-// Centroid indices grow with the register index, and a tile only replaces
-// the running best on a strictly larger score, so ties keep the lowest index.
-__device__ __forceinline__ void epilogue(const f32x16& acc, float& best, int& bidx, int base) {
-  const float tmax = max16(acc);
+// Running (max, argmax) update for one lane and one 32-centroid tile whose
+// maximum score is `tmax`.  `base` is the centroid index of accumulator
+// register 0 for this lane.  Centroid indices grow with the register index,
+// and a tile only replaces the running best on a strictly larger score, so
+// ties keep the lowest index.
+__device__ __forceinline__ void improve(const f32x16& acc, float tmax, float& best, int& bidx, int base) {
   if (tmax > best) {
     int r = 15;
 #pragma unroll
@@ -99,93 +120,107 @@ __device__ __forceinline__ void epilogue(const f32x16& acc, float& best, int& bi
   }
 }
 
-template <class T, int D, int PB>
-__global__ __launch_bounds__(256) void assign_kernel(const typename T::raw* __restrict__ X,
-                                                     const typename T::raw* __restrict__ Ch,
-                                                     const float* __restrict__ hb, int64_t N, int K,
-                                                     int32_t* __restrict__ labels, float* __restrict__ min_d2,
-                                                     double* __restrict__ part) {
-  using Cfg = AssignCfg<T, D, PB>;
-  constexpr int NCH = Cfg::NCH, HV = Cfg::HV, STEPS = Cfg::STEPS, PRE = Cfg::PRE;
+template <class T, int D, int PB, int W>
+__global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* __restrict__ X,
+                                                        const typename T::raw* __restrict__ Ch,
+                                                        const float* __restrict__ hb, int64_t N, int K, int B,
+                                                        int32_t* __restrict__ labels, float* __restrict__ min_d2,
+                                                        double* __restrict__ part) {
+  using Cfg = AssignCfg<T, D, PB, W>;
+  constexpr int NCH = Cfg::NCH, HV = Cfg::HV, STEPS = Cfg::STEPS, PRE = Cfg::PRE, NT = Cfg::THREADS;
+  constexpr int TK = Cfg::TK;
   __shared__ uint4 tile[2][Cfg::TILE_CH];
-  __shared__ __align__(16) float tb[2][kTileK];  // read back as float4
-  __shared__ double wsum[kAssignWaves];
+  __shared__ __align__(16) float tb[2][TK];  // read back as float4
+  __shared__ double wsum[W];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
-  const int b = blockIdx.y;
-  const typename T::raw* Xb = X + (int64_t)b * N * D;
-  const typename T::raw* Cb = Ch + (int64_t)b * K * D;
-  const float* hbb = hb + (int64_t)b * K;
-  const int64_t p0 = (int64_t)blockIdx.x * Cfg::ROWS + (int64_t)w * (PB * 32);
+  const int ntiles = (K + TK - 1) / TK;
+  const int64_t nblk = (N + Cfg::ROWS - 1) / Cfg::ROWS;  // point blocks per instance
 
-  // point fragments: lane half h holds dims [h*D/2, (h+1)*D/2) of point col
-  uint4 xf[PB][HV];
-#pragma unroll
-  for (int p = 0; p < PB; ++p) {
-    int64_t n = p0 + p * 32 + col;
-    n = n < N ? n : N - 1;
-    const uint4* src = reinterpret_cast<const uint4*>(Xb + n * D) + h * HV;
-#pragma unroll
-    for (int v = 0; v < HV; ++v) xf[p][v] = src[v];
-  }
+  // Persistent loop over (instance, point block).  Every workgroup does the
+  // same amount of work per block, so the workgroups resident on an XCD sweep
+  // the centroids in step and share each tile through that XCD's L2.
+  for (int64_t job = blockIdx.x; job < nblk * B; job += gridDim.x) {
+    const int b = (int)(job / nblk);
+    const int64_t blk = job - (int64_t)b * nblk;
+    const typename T::raw* Xb = X + (int64_t)b * N * D;
+    const typename T::raw* Cb = Ch + (int64_t)b * K * D;
+    const float* hbb = hb + (int64_t)b * K;
+    const int64_t p0 = blk * Cfg::ROWS + (int64_t)w * (PB * 32);
 
-  const int ntiles = (K + kTileK - 1) / kTileK;
-  uint4 pre[PRE];
-  float preb = 0.f;
-  auto load_tile = [&](int t) {
+    // point fragments: lane half h holds dims [h*D/2, (h+1)*D/2) of point col
+    uint4 xf[PB][HV];
 #pragma unroll
-    for (int i = 0; i < PRE; ++i) {
-      const int q = tid + 256 * i;
-      if (q < Cfg::TILE_CH) {
-        const int m = q / NCH, c = q % NCH;
-        const int k = t * kTileK + m;
-        pre[i] = k < K ? reinterpret_cast<const uint4*>(Cb + (int64_t)k * D)[c] : make_uint4(0, 0, 0, 0);
+    for (int p = 0; p < PB; ++p) {
+      int64_t n = p0 + p * 32 + col;
+      n = n < N ? n : N - 1;
+      const uint4* src = reinterpret_cast<const uint4*>(Xb + n * D) + h * HV;
+#pragma unroll
+      for (int v = 0; v < HV; ++v) xf[p][v] = src[v];
+    }
+
+    uint4 pre[PRE];
+    float preb = 0.f;
+    auto load_tile = [&](int t) {
+#pragma unroll
+      for (int i = 0; i < PRE; ++i) {
+        const int q = tid + NT * i;
+        if (q < Cfg::TILE_CH) {
+          const int m = q / NCH, c = q % NCH;
+          const int k = t * TK + m;
+          pre[i] = k < K ? reinterpret_cast<const uint4*>(Cb + (int64_t)k * D)[c] : make_uint4(0, 0, 0, 0);
+        }
       }
-    }
-    if (tid < kTileK) {
-      const int k = t * kTileK + tid;
-      preb = k < K ? hbb[k] : -INFINITY;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PRE; ++i) {
-      const int q = tid + 256 * i;
-      if (q < Cfg::TILE_CH) {
-        const int m = q / NCH, c = q % NCH;
-        tile[buf][m * NCH + (c ^ (m & (NCH - 1)))] = pre[i];
+      if (tid < TK) {
+        const int k = t * TK + tid;
+        preb = k < K ? hbb[k] : -INFINITY;
       }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < PRE; ++i) {
+        const int q = tid + NT * i;
+        if (q < Cfg::TILE_CH) {
+          const int m = q / NCH, c = q % NCH;
+          tile[buf][m * NCH + (c ^ (m & (NCH - 1)))] = pre[i];
+        }
+      }
+      if (tid < TK) tb[buf][tid] = preb;
+    };
+
+    float best[PB];
+    int bidx[PB];
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      best[p] = -INFINITY;
+      bidx[p] = 0;
     }
-    if (tid < kTileK) tb[buf][tid] = preb;
-  };
 
-  float best[PB];
-  int bidx[PB];
-#pragma unroll
-  for (int p = 0; p < PB; ++p) {
-    best[p] = -INFINITY;
-    bidx[p] = 0;
-  }
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-#pragma unroll
-    for (int sb = 0; sb < kTileK / 32; ++sb) {
+    // The centroid tile is consumed in groups of G sub-blocks of 32
+    // centroids: the G x PB accumulation chains of a group are issued
+    // interleaved step by step.  With kDelay the running max of the previous
+    // group is reduced on the vector ALU after the current group's MFMAs are
+    // issued, so it runs while they execute (`prev` starts at -inf, so the
+    // first reduction changes nothing).  With kPrefetchA the centroid
+    // fragments of the next group are read from LDS while the current group
+    // computes.
+    constexpr int G = Cfg::SBG;
+    constexpr int NG = TK / (32 * G);
+    auto read_frag = [&](int buf, int sb, uint4* af) {
       const int m = sb * 32 + col;
-      uint4 af[HV];
 #pragma unroll
       for (int v = 0; v < HV; ++v) {
         const int c = h * HV + v;
         af[v] = tile[buf][m * NCH + (c ^ (m & (NCH - 1)))];
       }
-      f32x16 bias;
+    };
+    auto read_bias = [&](int buf, int sb, f32x16& bias) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 bq = *reinterpret_cast<const float4*>(&tb[buf][sb * 32 + 8 * q + 4 * h]);
@@ -194,57 +229,140 @@ __global__ __launch_bounds__(256) void assign_kernel(const typename T::raw* __re
         bias[4 * q + 2] = bq.z;
         bias[4 * q + 3] = bq.w;
       }
-      const int base = t * kTileK + sb * 32 + 4 * h;
+    };
+    auto reduce_group = [&](const f32x16 (&a)[G][PB], int base) {
+      float tmax[G][PB];
+      bool any = false;
 #pragma unroll
-      for (int p = 0; p < PB; ++p) {
-        f32x16 acc = bias;
+      for (int j = 0; j < G; ++j)
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) acc = Mfma<T>::step(af, xf[p], st, acc);
-        epilogue(acc, best[p], bidx[p], base);
+        for (int p = 0; p < PB; ++p) {
+          tmax[j][p] = max16(a[j][p]);
+          any |= tmax[j][p] > best[p];
+        }
+      if (any) {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int p = 0; p < PB; ++p) improve(a[j][p], tmax[j][p], best[p], bidx[p], base + 32 * j);
       }
-    }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
-  }
+    };
 
-  // merge the two lane halves of each point: larger score, then lower index
-  double wacc = 0.0;
+    f32x16 prev[G][PB];
+    int prev_base = 0;
+    if constexpr (Cfg::DELAY) {
 #pragma unroll
-  for (int p = 0; p < PB; ++p) {
-    const float ob = __shfl_xor(best[p], 32);
-    const int oi = __shfl_xor(bidx[p], 32);
-    if (ob > best[p] || (ob == best[p] && oi < bidx[p])) {
-      best[p] = ob;
-      bidx[p] = oi;
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int p = 0; p < PB; ++p)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) prev[j][p][r] = -INFINITY;
     }
-    // squared distance to the chosen centroid, computed directly (no
-    // cancellation): each half sums its dims, the halves then add.
-    const uint4* cr = reinterpret_cast<const uint4*>(Cb + (int64_t)bidx[p] * D) + h * HV;
-    float part_d = 0.f;
+
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < ntiles) load_tile(t + 1);
+      uint4 afn[G][HV];
+      if constexpr (Cfg::APF) {
 #pragma unroll
-    for (int v = 0; v < HV; ++v) {
-      float xv[Vec<T>::N], cv[Vec<T>::N];
-      Vec<T>::unpack(xf[p][v], xv);
-      Vec<T>::unpack(cr[v], cv);
+        for (int j = 0; j < G; ++j) read_frag(buf, j, afn[j]);
+      }
 #pragma unroll
-      for (int e = 0; e < Vec<T>::N; ++e) {
-        const float df = xv[e] - cv[e];
-        part_d += df * df;
+      for (int g = 0; g < NG; ++g) {
+        uint4 af[G][HV];
+        if constexpr (Cfg::APF) {
+#pragma unroll
+          for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int v = 0; v < HV; ++v) af[j][v] = afn[j][v];
+          if (g + 1 < NG) {
+#pragma unroll
+            for (int j = 0; j < G; ++j) read_frag(buf, (g + 1) * G + j, afn[j]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < G; ++j) read_frag(buf, g * G + j, af[j]);
+        }
+        f32x16 acc[G][PB];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          f32x16 bias;
+          read_bias(buf, g * G + j, bias);
+#pragma unroll
+          for (int p = 0; p < PB; ++p) acc[j][p] = bias;
+        }
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+          for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int p = 0; p < PB; ++p) acc[j][p] = Mfma<T>::step(af[j], xf[p], st, acc[j][p]);
+        const int base = t * TK + g * G * 32 + 4 * h;
+        if constexpr (Cfg::DELAY) {
+          reduce_group(prev, prev_base);
+#pragma unroll
+          for (int i = 0; i < STEPS * PB * G; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          }
+#pragma unroll
+          for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int p = 0; p < PB; ++p) prev[j][p] = acc[j][p];
+          prev_base = base;
+        } else {
+          reduce_group(acc, base);
+        }
+      }
+      if (t + 1 < ntiles) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+    if constexpr (Cfg::DELAY) reduce_group(prev, prev_base);
+
+    // merge the two lane halves of each point: larger score, then lower index
+    double wacc = 0.0;
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      const float ob = __shfl_xor(best[p], 32);
+      const int oi = __shfl_xor(bidx[p], 32);
+      if (ob > best[p] || (ob == best[p] && oi < bidx[p])) {
+        best[p] = ob;
+        bidx[p] = oi;
+      }
+      // squared distance to the chosen centroid, computed directly (no
+      // cancellation): each half sums its dims, the halves then add.
+      const uint4* cr = reinterpret_cast<const uint4*>(Cb + (int64_t)bidx[p] * D) + h * HV;
+      float part_d = 0.f;
+#pragma unroll
+      for (int v = 0; v < HV; ++v) {
+        float xv[Vec<T>::N], cv[Vec<T>::N];
+        Vec<T>::unpack(xf[p][v], xv);
+        Vec<T>::unpack(cr[v], cv);
+#pragma unroll
+        for (int e = 0; e < Vec<T>::N; ++e) {
+          const float df = xv[e] - cv[e];
+          part_d += df * df;
+        }
+      }
+      const float other = __shfl_xor(part_d, 32);
+      const float d2 = h == 0 ? part_d + other : other + part_d;
+      const int64_t n = p0 + p * 32 + col;
+      if (h == 0 && n < N) {
+        labels[(int64_t)b * N + n] = bidx[p];
+        if (min_d2) min_d2[(int64_t)b * N + n] = d2;
+        wacc += (double)d2;
       }
     }
-    const float other = __shfl_xor(part_d, 32);
-    const float d2 = h == 0 ? part_d + other : other + part_d;
-    const int64_t n = p0 + p * 32 + col;
-    if (h == 0 && n < N) {
-      labels[(int64_t)b * N + n] = bidx[p];
-      if (min_d2) min_d2[(int64_t)b * N + n] = d2;
-      wacc += (double)d2;
+    wacc = wave_sum_f64(wacc);
+    if (lane == 0) wsum[w] = wacc;
+    __syncthreads();
+    if (tid == 0) {
+      double tot = 0.0;
+#pragma unroll
+      for (int i = 0; i < W; ++i) tot += wsum[i];
+      part[(int64_t)b * nblk + blk] = tot;
     }
   }
-  wacc = wave_sum_f64(wacc);
-  if (lane == 0) wsum[w] = wacc;
-  __syncthreads();
-  if (tid == 0) part[(int64_t)b * gridDim.x + blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
 }
 
 // inertia[b] = fixed-order sum of part[b, :]
@@ -280,30 +398,57 @@ hipError_t prep_t(const float* C, void* Chat, float* hb, int64_t rows, hipStream
   return hipGetLastError();
 }
 
-template <class T, int D, int PB>
+template <class T, int D, int PB, int W>
 hipError_t assign_t(const void* X, const void* Chat, const float* hb, int64_t N, int K, int B, int32_t* labels,
                     float* min_d2, double* part, hipStream_t s) {
-  using Cfg = AssignCfg<T, D, PB>;
-  const int64_t nwg = (N + Cfg::ROWS - 1) / Cfg::ROWS;
-  assign_kernel<T, D, PB><<<dim3((unsigned)nwg, (unsigned)B), dim3(256), 0, s>>>(
-      reinterpret_cast<const typename T::raw*>(X), reinterpret_cast<const typename T::raw*>(Chat), hb, N, K,
+  using Cfg = AssignCfg<T, D, PB, W>;
+  const int64_t jobs = (N + Cfg::ROWS - 1) / Cfg::ROWS * (int64_t)B;
+  // persistent grid: as many workgroups as fit on the device at once
+  static thread_local int cached_dev = -1, cached_slots = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev != cached_dev) {
+    int cus = 0, per_cu = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, assign_kernel<T, D, PB, W>, Cfg::THREADS, 0)) !=
+        hipSuccess)
+      return e;
+    cached_slots = cus * (per_cu > 0 ? per_cu : 1);
+    cached_dev = dev;
+  }
+  const int64_t grid = jobs < cached_slots ? jobs : cached_slots;
+  assign_kernel<T, D, PB, W><<<dim3((unsigned)grid), dim3(Cfg::THREADS), 0, s>>>(
+      reinterpret_cast<const typename T::raw*>(X), reinterpret_cast<const typename T::raw*>(Chat), hb, N, K, B,
       labels, min_d2, part);
   return hipGetLastError();
 }
 
-// Register blocking allowed per row size: the point fragments of PB blocks
-// take PB * D * SZ / 8 VGPRs per lane.
+// Compiled configurations.  The point fragments of PB blocks take
+// PB * D * SZ / 8 VGPRs per lane, so deep blocking is limited to short rows.
+constexpr bool cfg_compiled(int row_bytes, int pb, int waves) {
+  if (pb == 1 && (waves == 4 || waves == 8)) return true;
+  if (pb == 2 && (waves == 4 || waves == 8)) return row_bytes <= 512;
+  if (pb == 4 && waves == 4) return row_bytes <= 256;
+  return false;
+}
+
 template <class T, int D>
-hipError_t assign_pb(int pb, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
-                     int32_t* labels, float* min_d2, double* part, hipStream_t s) {
+hipError_t assign_cfg(AssignConfig c, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
+                      int32_t* labels, float* min_d2, double* part, hipStream_t s) {
   constexpr int rb = D * T::SZ;
-  if constexpr (rb <= 256) {
-    if (pb >= 4) return assign_t<T, D, 4>(X, Chat, hb, N, K, B, labels, min_d2, part, s);
+#define FKM_CASE(PB_, W_)                                                                \
+  if constexpr (cfg_compiled(rb, PB_, W_)) {                                             \
+    if (c.pb == PB_ && c.waves == W_)                                                    \
+      return assign_t<T, D, PB_, W_>(X, Chat, hb, N, K, B, labels, min_d2, part, s);     \
   }
-  if constexpr (rb <= 512) {
-    if (pb >= 2) return assign_t<T, D, 2>(X, Chat, hb, N, K, B, labels, min_d2, part, s);
-  }
-  return assign_t<T, D, 1>(X, Chat, hb, N, K, B, labels, min_d2, part, s);
+  FKM_CASE(4, 4)
+  FKM_CASE(2, 8)
+  FKM_CASE(2, 4)
+  FKM_CASE(1, 8)
+  FKM_CASE(1, 4)
+#undef FKM_CASE
+  return hipErrorInvalidValue;
 }
 
 template <template <class, int> class F, class... A>
@@ -333,32 +478,52 @@ template <class T, int D> struct PrepF {
   }
 };
 template <class T, int D> struct AssignF {
-  static hipError_t run(int pb, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
+  static hipError_t run(AssignConfig c, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
                         int32_t* labels, float* min_d2, double* part, hipStream_t s) {
-    return assign_pb<T, D>(pb, X, Chat, hb, N, K, B, labels, min_d2, part, s);
+    return assign_cfg<T, D>(c, X, Chat, hb, N, K, B, labels, min_d2, part, s);
   }
 };
 
 }  // namespace
 
-int assign_pick_pb(int dt, int D, int64_t N, int B) {
-  const int row_bytes = D * dtype_size(dt);
-  const int maxpb = row_bytes <= 256 ? 4 : row_bytes <= 512 ? 2 : 1;
-  // prefer the deepest register blocking that still gives >= 4 workgroups per CU
-  for (int pb = maxpb; pb > 1; pb >>= 1) {
-    const int64_t wgs = (N + assign_rows_per_wg(pb) - 1) / assign_rows_per_wg(pb) * (int64_t)B;
-    if (wgs >= 1024) return pb;
+namespace {
+// FLASHKM_ASSIGN_CONFIG="pb,waves", parsed once; {0,0} when unset or malformed.
+AssignConfig env_override() {
+  static const AssignConfig c = [] {
+    AssignConfig r{0, 0};
+    if (const char* e = getenv("FLASHKM_ASSIGN_CONFIG")) {
+      int pb = 0, w = 0;
+      if (sscanf(e, "%d,%d", &pb, &w) == 2) r = AssignConfig{pb, w};
+    }
+    return r;
+  }();
+  return c;
+}
+}  // namespace
+
+AssignConfig assign_pick(int dt, int D, int64_t N, int B) {
+  const int rb = D * dtype_size(dt);
+  const AssignConfig o = env_override();
+  if (o.pb && cfg_compiled(rb, o.pb, o.waves)) return o;
+  // Two waves per SIMD (8-wave workgroups) so one wave's argmax epilogue
+  // overlaps the other's MFMAs; the deepest register blocking that still
+  // leaves >= 4 workgroups per CU.
+  const AssignConfig order[] = {{2, 8}, {1, 8}, {1, 4}};
+  for (const AssignConfig& c : order) {
+    if (!cfg_compiled(rb, c.pb, c.waves)) continue;
+    const int64_t wgs = (N + c.rows() - 1) / c.rows() * (int64_t)B;
+    if (wgs >= 1024) return c;
   }
-  return 1;
+  return AssignConfig{1, 4};
 }
 
 hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t rows, hipStream_t s) {
   return dispatch_dt_d<PrepF>(dt, D, C, Chat, hb, rows, s);
 }
 
-hipError_t launch_assign(int dt, int D, int pb, const void* X, const void* Chat, const float* hb, int64_t N, int K,
-                         int B, int32_t* labels, float* min_d2, double* part, hipStream_t s) {
-  return dispatch_dt_d<AssignF>(dt, D, pb, X, Chat, hb, N, K, B, labels, min_d2, part, s);
+hipError_t launch_assign(int dt, int D, AssignConfig cfg, const void* X, const void* Chat, const float* hb, int64_t N,
+                         int K, int B, int32_t* labels, float* min_d2, double* part, hipStream_t s) {
+  return dispatch_dt_d<AssignF>(dt, D, cfg, X, Chat, hb, N, K, B, labels, min_d2, part, s);
 }
 
 hipError_t launch_inertia_reduce(const double* part, int nwg, int B, double* inertia, double* hist, bool accumulate,

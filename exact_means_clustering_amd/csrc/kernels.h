@@ -13,12 +13,19 @@ enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : 2; }
 
 // ---- assignment stage ------------------------------------------------------
-// Points per workgroup of the assign kernel for a given point-block count.
-constexpr int kAssignWaves = 4;
-inline int assign_rows_per_wg(int pb) { return kAssignWaves * 32 * pb; }
-// Point blocks (32 points each) per wave chosen for a shape.
-int assign_pick_pb(int dt, int D, int64_t N, int B);
-// Largest number of assign workgroups per instance over every pick.
+// Tile configuration of the assign kernel: `pb` blocks of 32 points held in
+// registers per wave, `waves` waves per workgroup sharing one LDS centroid
+// tile.  A workgroup covers waves * 32 * pb points.
+struct AssignConfig {
+  int pb;
+  int waves;
+  int rows() const { return waves * 32 * pb; }
+};
+// Configuration for a shape (dtype, D, N per instance, B instances).  The
+// environment variable FLASHKM_ASSIGN_CONFIG="pb,waves" overrides the choice
+// when that pair is compiled for the row size (tuning only).
+AssignConfig assign_pick(int dt, int D, int64_t N, int B);
+// Largest number of assign workgroups per instance over every configuration.
 inline int64_t assign_max_wgs(int64_t N) { return (N + 127) / 128; }
 
 // Chat[r] = RNE(C[r] -> dtype), hb[r] = -0.5 * ||Chat[r]||^2 for r < rows.
@@ -26,8 +33,8 @@ hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int
 
 // Fused distance + running argmin.  part[b * nwg + wg] receives each
 // workgroup's fp64 sum of min_d2 (nwg = ceil(N / rows_per_wg(pb))).
-hipError_t launch_assign(int dt, int D, int pb, const void* X, const void* Chat, const float* hb, int64_t N,
-                         int K, int B, int32_t* labels, float* min_d2, double* part, hipStream_t s);
+hipError_t launch_assign(int dt, int D, AssignConfig cfg, const void* X, const void* Chat, const float* hb,
+                         int64_t N, int K, int B, int32_t* labels, float* min_d2, double* part, hipStream_t s);
 
 // inertia[b] = sum_w part[b * nwg + w] in a fixed order (added to the old
 // value when `accumulate`); also copied to hist[b] if non-null.

@@ -140,10 +140,10 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
       if (c + 1 < nch)
         if (int rc = h2d(c + 1)) return rc;
       KS_HIP(hipStreamWaitEvent(r.cs, r.copied[sl], 0), "stream wait");
-      const int pb = assign_pick_pb(dtype, D, rows, 1);
-      KS_HIP(launch_assign(dtype, D, pb, xslot[sl], w.chat, w.hb, rows, K, 1, lslot[sl], nullptr, w.part, r.cs),
+      const AssignConfig cfg = assign_pick(dtype, D, rows, 1);
+      KS_HIP(launch_assign(dtype, D, cfg, xslot[sl], w.chat, w.hb, rows, K, 1, lslot[sl], nullptr, w.part, r.cs),
              "assign launch");
-      const int64_t nwg = (rows + assign_rows_per_wg(pb) - 1) / assign_rows_per_wg(pb);
+      const int64_t nwg = (rows + cfg.rows() - 1) / cfg.rows();
       KS_HIP(launch_inertia_reduce(w.part, (int)nwg, 1, J_dev + t, nullptr, true, r.cs), "inertia launch");
       const uint32_t* skeys = nullptr;
       const uint32_t* perm = nullptr;
