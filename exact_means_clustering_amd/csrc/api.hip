@@ -59,8 +59,9 @@ int run_update(const void* X, int dt, int64_t N, int D, int B, const int32_t* la
   const int64_t n = N * B;
   const uint32_t nseg = (uint32_t)((int64_t)B * K);
   KM_HIP(launch_argsort_labels(labels, N, B, K, w.sort, &skeys, &perm, s), "argsort launch");
-  KM_HIP(launch_segment_offsets(skeys, n, nseg, w.off, s), "segment offsets launch");
   SegOut o{C_prev, C_new, counts ? counts : w.cnt, nullptr, nullptr};
+  const EmptyOut eo{C_prev, C_new, o.counts, D};
+  KM_HIP(launch_segment_offsets(skeys, n, nseg, w.off, eo, s), "segment offsets launch");
   KM_HIP(launch_segment_reduce(dt, D, X, perm, skeys, w.off, n, nseg, o, w.seg, s), "segment reduce launch");
   return KM_OK;
 }

@@ -365,19 +365,23 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
   }
 }
 
-// inertia[b] = fixed-order sum of part[b, :]
-__global__ __launch_bounds__(256) void inertia_reduce_kernel(const double* __restrict__ part, int nwg,
-                                                             double* __restrict__ inertia, double* __restrict__ hist,
-                                                             int accumulate) {
-  __shared__ double ws[4];
+// inertia[b] = fixed-order sum of part[b, :] (1024 threads, strided, then a
+// fixed tree)
+__global__ __launch_bounds__(1024) void inertia_reduce_kernel(const double* __restrict__ part, int nwg,
+                                                              double* __restrict__ inertia,
+                                                              double* __restrict__ hist, int accumulate) {
+  __shared__ double ws[16];
   const int b = blockIdx.x;
   double v = 0.0;
-  for (int i = threadIdx.x; i < nwg; i += 256) v += part[(int64_t)b * nwg + i];
+#pragma unroll 8
+  for (int i = threadIdx.x; i < nwg; i += 1024) v += part[(int64_t)b * nwg + i];
   v = wave_sum_f64(v);
   if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
   __syncthreads();
   if (threadIdx.x == 0) {
-    double tot = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+    double tot = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot += ws[i];
     if (accumulate) tot += inertia[b];
     inertia[b] = tot;
     if (hist) hist[b] = tot;
@@ -528,7 +532,7 @@ hipError_t launch_assign(int dt, int D, AssignConfig cfg, const void* X, const v
 
 hipError_t launch_inertia_reduce(const double* part, int nwg, int B, double* inertia, double* hist, bool accumulate,
                                  hipStream_t s) {
-  inertia_reduce_kernel<<<dim3((unsigned)B), dim3(256), 0, s>>>(part, nwg, inertia, hist, accumulate ? 1 : 0);
+  inertia_reduce_kernel<<<dim3((unsigned)B), dim3(1024), 0, s>>>(part, nwg, inertia, hist, accumulate ? 1 : 0);
   return hipGetLastError();
 }
 

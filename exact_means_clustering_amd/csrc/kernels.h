@@ -55,13 +55,25 @@ struct SortBuffers {
 // *sorted_keys / *perm point at the buffers holding the result.
 hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K, SortBuffers& buf,
                                  const uint32_t** sorted_keys, const uint32_t** perm, hipStream_t s);
+// Empty-cluster output of the offsets pass: when counts is non-null, every
+// key no row carries gets counts[k] = 0 and C_new[k] = C_prev[k] (D floats).
+struct EmptyOut {
+  const float* C_prev;
+  float* C_new;
+  int32_t* counts;
+  int D;
+};
 // off[k] = #{rows with key < k} for k in [0, nseg]
 hipError_t launch_segment_offsets(const uint32_t* sorted_keys, int64_t n, uint32_t nseg, int32_t* off,
-                                  hipStream_t s);
+                                  const EmptyOut& eo, hipStream_t s);
 
 // ---- segment-local reductions ----------------------------------------------
+#ifndef FKM_SEG_ROWS
 constexpr int kSegRows = 256;    // rows of the sorted order per wave chunk (level 1)
-constexpr int kSegGroup = 32;    // level-1 chunks per level-2 group
+#else
+constexpr int kSegRows = FKM_SEG_ROWS;
+#endif
+constexpr int kSegGroup = 8;     // level-1 chunks per level-2 group
 inline int64_t seg_chunks(int64_t n) { return (n + kSegRows - 1) / kSegRows; }
 inline int64_t seg_groups(int64_t n) { return (seg_chunks(n) + kSegGroup - 1) / kSegGroup; }
 

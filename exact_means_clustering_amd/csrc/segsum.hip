@@ -14,8 +14,8 @@
 //   level 2  one wave per group of kSegGroup chunks adds (fp64) the chunk
 //            fragments of every segment that crosses a chunk edge; segments
 //            inside the group are finished, the others leave group fragments.
-//   level 3  one wave per group finishes the segment (if any) that crosses
-//            into the group from the left and ends inside it.
+//   level 3  the segment (if any) that crosses into a group from the left
+//            and ends inside it is finished by a workgroup of 16 waves.
 // Every segment is finished by exactly one wave in a fixed order, so the
 // update is deterministic and uses no atomics.  Fragment slot rule (used to
 // find a segment's piece in unit u of size U): the piece is in slot 1 iff u
@@ -54,89 +54,145 @@ __device__ __forceinline__ void finish(const SegOut& o, int64_t k, int D, int la
 }
 
 // ---------------------------------------------------------------------------
-// level 1: gather + fp32 sums per chunk
+// level 1: streaming gather + fp32 segmented sums per chunk
 // ---------------------------------------------------------------------------
+// One wave per chunk of kSegRows sorted positions.  The chunk's keys and row
+// ids are staged in LDS; the wave walks the chunk in steps of SL rows (one
+// row per lane slot, LPR lanes per row) and keeps kRing steps of row loads
+// in flight whatever the segment boundaries.  Each lane slot accumulates its
+// rows of the current segment in fp32; when the (wave-uniform) key changes,
+// the slots are combined in a fixed butterfly and the piece is emitted:
+// finished on the spot if the whole segment lies in the chunk, otherwise
+// stored as the chunk's fragment (slot 0: the chunk's first segment, slot 1:
+// its last).
+#ifndef FKM_RING
+constexpr int kRing = 8;   // steps of row loads kept in flight per wave
+#else
+constexpr int kRing = FKM_RING;
+#endif
+
 template <class T, int D>
 __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* __restrict__ X,
                                                          const uint32_t* __restrict__ perm,
-                                                         const uint32_t* __restrict__ keys,
-                                                         const int32_t* __restrict__ off, int64_t n, SegOut o,
+                                                         const uint32_t* __restrict__ keys, int64_t n, SegOut o,
                                                          float* __restrict__ frag) {
   constexpr int VEC = Vec<T>::N;           // elements per 16-byte word
   constexpr int LPR = D * T::SZ / 16;      // lanes per row
-  constexpr int SL = 64 / LPR;             // rows in flight per wave
-  static_assert(LPR >= 1 && LPR <= 64, "row size");
+  constexpr int SL = 64 / LPR;             // rows per step (lane slots)
+  constexpr int U = kSegRows;
+  static_assert(LPR >= 1 && LPR <= 64 && U % SL == 0, "row size");
+  __shared__ uint32_t skey[4][U];
+  __shared__ uint32_t srow[4][U];
   const int lane = lane_id();
-  const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t r0 = c * kSegRows;
-  if (r0 >= n) return;
-  const int64_t r1 = r0 + kSegRows < n ? r0 + kSegRows : n;
+  const int w = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 4 + w;
+  const int64_t r0 = c * U;
+  const bool active = r0 < n;
+  const int cnt = active ? (int)(n - r0 < U ? n - r0 : U) : 0;
+  for (int e = lane; e < U; e += 64) {
+    skey[w][e] = e < cnt ? keys[r0 + e] : 0xFFFFFFFFu;
+    srow[w][e] = e < cnt ? perm[r0 + e] : 0u;
+  }
+  __syncthreads();
+  if (!active) return;
   const int q = lane / LPR, g = lane % LPR;
-  const int64_t kf = keys[r0], kl = keys[r1 - 1];
+  const uint32_t kf = skey[w][0], kl = skey[w][cnt - 1];
+  // does the chunk's first (last) segment continue from the previous (into the next) chunk?
+  const bool cont_left = r0 > 0 && keys[r0 - 1] == kf;
+  const bool cont_right = r0 + cnt < n && keys[r0 + cnt] == kl;
+  const int nsteps = (cnt + SL - 1) / SL;
 
-  for (int64_t k = kf; k <= kl; ++k) {
-    const int64_t s = off[k], e = off[k + 1];
-    const int64_t a = s > r0 ? s : r0;
-    const int64_t z = e < r1 ? e : r1;
-    if (a >= z) continue;
-    float acc[VEC];
+  auto load_step = [&](int i) -> uint4 {
+    const int j = i * SL + q;
+    if (i < nsteps && j < cnt) return reinterpret_cast<const uint4*>(X + (int64_t)srow[w][j] * D)[g];
+    return make_uint4(0, 0, 0, 0);
+  };
+
+  float acc[VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    int64_t j = a + q;
-    // four rows per lane in flight
-    for (; j + 3 * SL < z; j += 4 * SL) {
-      uint4 v[4];
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  uint32_t cur = kf;
+  int seg_start = 0;
+  // emit the piece of segment k that ends before row `end` of the chunk
+  auto flush = [&](uint32_t k, int end) {
+    float s[VEC];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t row = perm[j + u * SL];
-        v[u] = reinterpret_cast<const uint4*>(X + (int64_t)row * D)[g];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float f[VEC];
-        Vec<T>::unpack(v[u], f);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[i] += f[i];
-      }
-    }
-    for (; j < z; j += SL) {
-      const uint32_t row = perm[j];
-      float f[VEC];
-      Vec<T>::unpack(reinterpret_cast<const uint4*>(X + (int64_t)row * D)[g], f);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] += f[i];
-    }
-    // combine the SL row slots (fixed butterfly order)
+    for (int e = 0; e < VEC; ++e) s[e] = acc[e];
 #pragma unroll
     for (int o2 = LPR; o2 < 64; o2 <<= 1)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] += __shfl_xor(acc[i], o2);
+      for (int e = 0; e < VEC; ++e) s[e] += __shfl_xor(s[e], o2);
+    const bool left = k == kf && cont_left;
+    const bool right = k == kl && cont_right;
     if (q == 0) {
-      if (s >= r0 && e <= r1) {
-        const int64_t cnt = e - s;
+      if (!left && !right) {
+        const int64_t nk = end - seg_start;
         if (o.S_acc) {
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) o.S_acc[k * D + g * VEC + i] += (double)acc[i];
-          if (g == 0) o.n_acc[k] += cnt;
+          for (int e = 0; e < VEC; ++e) o.S_acc[(int64_t)k * D + g * VEC + e] += (double)s[e];
+          if (g == 0) o.n_acc[k] += nk;
         } else {
-          const float fc = (float)cnt;
+          const float fc = (float)nk;
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) o.C_new[k * D + g * VEC + i] = acc[i] / fc;
-          if (g == 0) o.counts[k] = (int32_t)cnt;
+          for (int e = 0; e < VEC; ++e) o.C_new[(int64_t)k * D + g * VEC + e] = s[e] / fc;
+          if (g == 0) o.counts[k] = (int32_t)nk;
         }
       } else {
-        const int slot = (k == kf) ? 0 : 1;
-        float* fp = frag + (c * 2 + slot) * D + g * VEC;
+        float* fp = frag + (c * 2 + (k == kf ? 0 : 1)) * D + g * VEC;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) fp[i] = acc[i];
+        for (int e = 0; e < VEC; ++e) fp[e] = s[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    seg_start = end;
+  };
+
+  uint4 ring[kRing];
+#pragma unroll
+  for (int u = 0; u < kRing; ++u) ring[u] = load_step(u);
+  for (int i0 = 0; i0 < nsteps; i0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int i = i0 + u;
+      if (i < nsteps) {
+        const uint4 v = ring[u];
+        ring[u] = load_step(i + kRing);
+        float f[VEC];
+        Vec<T>::unpack(v, f);
+        const int j = i * SL + q;
+        const bool valid = j < cnt;
+        const uint32_t mk = valid ? skey[w][j] : 0xFFFFFFFFu;
+        const int jl = (i * SL + SL < cnt ? i * SL + SL : cnt) - 1;
+        const uint32_t lk = skey[w][jl];  // key of the step's last row (wave-uniform)
+        if (lk == cur) {
+          // whole step inside the current segment (rows past the end hold zeros)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[e] += f[e];
+        } else {
+          // the step ends `cur` and starts one or more new segments
+          for (;;) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] += mk == cur ? f[e] : 0.f;
+            if (cur == lk) break;
+            const uint64_t above = __ballot(valid && mk > cur);
+            const int fl = __ffsll((unsigned long long)above) - 1;
+            flush(cur, i * SL + fl / LPR);
+            cur = __shfl(mk, fl);
+          }
+        }
       }
     }
   }
+  flush(cur, cnt);
 }
 
 // ---------------------------------------------------------------------------
 // level 2: per group of chunks, combine chunk fragments (fp64)
 // ---------------------------------------------------------------------------
+// One wave per group.  The group's segments are scanned 64 at a time (one
+// coalesced load of their offsets); a ballot picks the ones that cross a
+// chunk edge, and only those are summed.
 template <int D>
 __global__ __launch_bounds__(256) void seg_level2_kernel(const uint32_t* __restrict__ keys,
                                                          const int32_t* __restrict__ off, int64_t n, SegOut o,
@@ -150,94 +206,115 @@ __global__ __launch_bounds__(256) void seg_level2_kernel(const uint32_t* __restr
   if (gr0 >= n) return;
   const int64_t gr1 = gr0 + UG < n ? gr0 + UG : n;
   const int64_t kf = keys[gr0], kl = keys[gr1 - 1];
-  for (int64_t k = kf; k <= kl; ++k) {
-    const int64_t s = off[k], e = off[k + 1];
-    if (s >= e) continue;
-    if (s / U == (e - 1) / U) continue;  // finished at level 1
-    const int64_t a = s > gr0 ? s : gr0;
-    const int64_t z = e < gr1 ? e : gr1;
-    if (a >= z) continue;
-    double acc[PER];
+  for (int64_t k0 = kf; k0 <= kl; k0 += 64) {
+    const int64_t kk = k0 + lane;
+    const bool valid = kk <= kl;
+    const int64_t sv = valid ? off[kk] : 0, ev = valid ? off[kk + 1] : 0;
+    // crosses a chunk edge (a segment inside one chunk was finished at level 1)
+    const bool cross = valid && sv < ev && (sv / U != (ev - 1) / U);
+    uint64_t mask = __ballot(cross);
+    while (mask) {
+      const int j = __ffsll((unsigned long long)mask) - 1;
+      mask &= mask - 1;
+      const int64_t k = k0 + j;
+      const int64_t s = __shfl(sv, j), e = __shfl(ev, j);
+      const int64_t a = s > gr0 ? s : gr0;
+      const int64_t z = e < gr1 ? e : gr1;
+      double acc[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = 0.0;
-    const int64_t u0 = a / U, u1 = (z - 1) / U;
+      for (int q = 0; q < PER; ++q) acc[q] = 0.0;
+      const int64_t u0 = a / U, u1 = (z - 1) / U;
 #pragma unroll 4
-    for (int64_t u = u0; u <= u1; ++u) {
-      const float* fp = frag + (u * 2 + frag_slot(u, U, s)) * D;
+      for (int64_t u = u0; u <= u1; ++u) {
+        const float* fp = frag + (u * 2 + frag_slot(u, U, s)) * D;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int d = lane + 64 * j;
-        if (d < D) acc[j] += (double)fp[d];
+        for (int q = 0; q < PER; ++q) {
+          const int d = lane + 64 * q;
+          if (d < D) acc[q] += (double)fp[d];
+        }
       }
-    }
-    if (s >= gr0 && e <= gr1) {
-      finish<PER>(o, k, D, lane, acc, e - s);
-    } else {
-      double* gp = gfrag + (g * 2 + ((k == kf) ? 0 : 1)) * D;
+      if (s >= gr0 && e <= gr1) {
+        finish<PER>(o, k, D, lane, acc, e - s);
+      } else {
+        double* gp = gfrag + (g * 2 + ((k == kf) ? 0 : 1)) * D;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int d = lane + 64 * j;
-        if (d < D) gp[d] = acc[j];
+        for (int q = 0; q < PER; ++q) {
+          const int d = lane + 64 * q;
+          if (d < D) gp[d] = acc[q];
+        }
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// level 3: the segment crossing into group g from the left and ending in it
+// level 3: segments that cross a group edge
 // ---------------------------------------------------------------------------
+// A segment crossing into group g from the left and ending in it is owned by
+// g.  One workgroup of kL3Waves waves covers kL3Waves groups: each wave checks
+// its group's ownership, then all waves sum each owned segment's group
+// fragments together (interleaved by wave, combined in wave order).
+constexpr int kL3Waves = 16;
 template <int D>
-__global__ __launch_bounds__(256) void seg_level3_kernel(const uint32_t* __restrict__ keys,
-                                                         const int32_t* __restrict__ off, int64_t n, SegOut o,
-                                                         const double* __restrict__ gfrag) {
+__global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint32_t* __restrict__ keys,
+                                                                   const int32_t* __restrict__ off, int64_t n,
+                                                                   int64_t ngroups, SegOut o,
+                                                                   const double* __restrict__ gfrag) {
   constexpr int PER = (D + 63) / 64;
   constexpr int64_t UG = (int64_t)kSegRows * kSegGroup;
-  __shared__ double part[4][PER * 64];
+  __shared__ double part[kL3Waves][PER * 64];
+  __shared__ int64_t own_k[kL3Waves], own_s[kL3Waves], own_e[kL3Waves];
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
-  const int64_t g = blockIdx.x;
-  const int64_t gr0 = g * UG;
-  const int64_t gr1 = gr0 + UG < n ? gr0 + UG : n;
-  const int64_t k = keys[gr0];
-  const int64_t s = off[k], e = off[k + 1];
-  if (!(s < gr0 && e <= gr1)) return;  // uniform over the workgroup
-  // the four waves take interleaved groups; partials combine in a fixed order
-  const int64_t g0 = s / UG;
-  double acc[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) acc[j] = 0.0;
-#pragma unroll 2
-  for (int64_t gg = g0 + w; gg <= g; gg += 4) {
-    const double* gp = gfrag + (gg * 2 + frag_slot(gg, UG, s)) * D;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int d = lane + 64 * j;
-      if (d < D) acc[j] += gp[d];
+  if (lane == 0) {
+    const int64_t g = (int64_t)blockIdx.x * kL3Waves + w;
+    int64_t k = -1, s = 0, e = 0;
+    if (g < ngroups) {
+      const int64_t gr0 = g * UG;
+      const int64_t gr1 = gr0 + UG < n ? gr0 + UG : n;
+      const int64_t kk = keys[gr0];
+      s = off[kk];
+      e = off[kk + 1];
+      if (s < gr0 && e <= gr1) k = kk;
     }
+    own_k[w] = k;
+    own_s[w] = s;
+    own_e[w] = e;
   }
-#pragma unroll
-  for (int j = 0; j < PER; ++j) part[w][lane + 64 * j] = acc[j];
   __syncthreads();
-  if (w == 0) {
+  for (int ow = 0; ow < kL3Waves; ++ow) {
+    const int64_t k = own_k[ow];
+    if (k < 0) continue;  // uniform over the workgroup
+    const int64_t s = own_s[ow], e = own_e[ow];
+    const int64_t g_end = (int64_t)blockIdx.x * kL3Waves + ow;
+    double acc[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int d = lane + 64 * j;
-      acc[j] = (part[0][d] + part[1][d]) + (part[2][d] + part[3][d]);
+    for (int q = 0; q < PER; ++q) acc[q] = 0.0;
+#pragma unroll 4
+    for (int64_t gg = s / UG + w; gg <= g_end; gg += kL3Waves) {
+      const double* gp = gfrag + (gg * 2 + frag_slot(gg, UG, s)) * D;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int d = lane + 64 * q;
+        if (d < D) acc[q] += gp[d];
+      }
     }
-    finish<PER>(o, k, D, lane, acc, e - s);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) part[w][lane + 64 * q] = acc[q];
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int d = lane + 64 * q;
+        double v = 0.0;
+#pragma unroll
+        for (int i = 0; i < kL3Waves; ++i) v += part[i][d];
+        acc[q] = v;
+      }
+      finish<PER>(o, k, D, lane, acc, e - s);
+    }
+    __syncthreads();
   }
-}
-
-// empty segments: C_new[k] = C_prev[k], counts[k] = 0 (means mode only)
-__global__ __launch_bounds__(256) void seg_empty_kernel(const int32_t* __restrict__ off, int64_t nseg, int D,
-                                                        const float* __restrict__ C_prev, float* __restrict__ C_new,
-                                                        int32_t* __restrict__ counts) {
-  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (k >= nseg) return;
-  if (off[k + 1] > off[k]) return;
-  counts[k] = 0;
-  if (C_new != C_prev)
-    for (int d = 0; d < D; ++d) C_new[k * D + d] = C_prev[k * D + d];
 }
 
 __global__ __launch_bounds__(256) void mean_from_sums_kernel(const double* __restrict__ S,
@@ -263,15 +340,14 @@ hipError_t seg_reduce_t(const void* X, const uint32_t* perm, const uint32_t* key
   const int64_t nchunks = seg_chunks(n);
   const int64_t ngroups = seg_groups(n);
   seg_level1_kernel<T, D><<<dim3((unsigned)((nchunks + 3) / 4)), dim3(256), 0, s>>>(
-      reinterpret_cast<const typename T::raw*>(X), perm, keys, off, n, o, buf.frag);
+      reinterpret_cast<const typename T::raw*>(X), perm, keys, n, o, buf.frag);
   if (nchunks > 1) {
     seg_level2_kernel<D><<<dim3((unsigned)((ngroups + 3) / 4)), dim3(256), 0, s>>>(keys, off, n, o, buf.frag,
                                                                                   buf.gfrag);
-    if (ngroups > 1) seg_level3_kernel<D><<<dim3((unsigned)ngroups), dim3(256), 0, s>>>(keys, off, n, o, buf.gfrag);
+    if (ngroups > 1)
+      seg_level3_kernel<D><<<dim3((unsigned)((ngroups + kL3Waves - 1) / kL3Waves)), dim3(kL3Waves * 64), 0, s>>>(
+          keys, off, n, ngroups, o, buf.gfrag);
   }
-  if (!o.S_acc)
-    seg_empty_kernel<<<dim3((unsigned)((nseg + 255) / 256)), dim3(256), 0, s>>>(off, nseg, D, o.C_prev, o.C_new,
-                                                                               o.counts);
   return hipGetLastError();
 }
 

@@ -10,9 +10,10 @@
 //   scatter stable rank of every key inside its workgroup tile, written to
 //           digit base + workgroup offset + rank.
 // Ranks come from wave-level digit matching (eight ballots give each lane the
-// mask of lanes holding the same digit), so there are no atomics on hot
-// digits and the output order is fully determined: equal keys keep their row
-// order.  No workgroup ever waits on another.
+// mask of lanes holding the same digit) and per-wave counters, so the output
+// order is fully determined: equal keys keep their row order.  Histogram
+// counts use LDS atomics (exact integers, so order-free).  No workgroup ever
+// waits on another.
 #include "common.h"
 #include "kernels.h"
 
@@ -64,19 +65,19 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(KeyFn key, int64_t n, in
                                                         int64_t nblk) {
   __shared__ uint32_t cnt[256];
   const int t = threadIdx.x;
-  const int lane = t & 63;
   cnt[t] = 0;
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * kSortTile;
-#pragma unroll 4
+  uint32_t d[kIPT];
+#pragma unroll
   for (int r = 0; r < kIPT; ++r) {
     const int64_t i = base + r * kT + t;
-    const bool valid = i < n;
-    const uint32_t d = valid ? (key(i) >> shift) & 255u : 0u;
-    const uint64_t m = match_digit(d, valid);
-    // the lowest lane of each digit group adds the group size
-    if (valid && (m & ((1ull << lane) - 1ull)) == 0) atomicAdd(&cnt[d], (uint32_t)__popcll(m));
+    d[r] = i < n ? (key(i) >> shift) & 255u : 256u;
   }
+  // LDS atomics: the counts are exact integers, so their order is irrelevant
+#pragma unroll
+  for (int r = 0; r < kIPT; ++r)
+    if (d[r] < 256u) atomicAdd(&cnt[d[r]], 1u);
   __syncthreads();
   hist[(int64_t)t * nblk + blockIdx.x] = cnt[t];
 }
@@ -112,73 +113,124 @@ __global__ __launch_bounds__(kT) void radix_scan_kernel(uint32_t* __restrict__ h
   if (threadIdx.x == 0) dtot[blockIdx.x] = running;
 }
 
+// Stable scatter of one tile.  Each wave ranks a contiguous quarter of the
+// tile (64 keys per round, in row order): a key's rank among equal digits of
+// its wave = keys of that digit in the wave's earlier rounds (a per-wave LDS
+// counter; LDS operations of one wave complete in order, so no barrier is
+// needed between rounds) + equal digits in lower lanes.  One barrier later
+// the per-wave counts become per-wave offsets, every key lands in an LDS copy
+// of the tile sorted by digit, and the tile is written out digit run by digit
+// run, so consecutive threads write consecutive addresses.
 template <class KeyFn>
 __global__ __launch_bounds__(kT) void radix_scatter_kernel(KeyFn key, const uint32_t* __restrict__ vals_in, int64_t n,
                                                            int shift, const uint32_t* __restrict__ hist,
                                                            const uint32_t* __restrict__ dtot, int64_t nblk,
                                                            uint32_t* __restrict__ keys_out,
                                                            uint32_t* __restrict__ vals_out) {
-  __shared__ uint32_t dbase[256];
-  __shared__ uint32_t running[256];
-  __shared__ uint32_t wc[2][4][256];  // per round parity, per wave, per digit: count | (round+1) << 16
+  constexpr int KW = kSortTile / 4;   // keys per wave
+  constexpr int RW = KW / 64;         // rounds per wave
+  __shared__ uint32_t lkey[kSortTile];
+  __shared__ uint32_t lval[kSortTile];
+  __shared__ uint32_t gbase[256];     // global position of LDS slot 0 of digit d's run, minus lstart[d]
+  __shared__ uint32_t lstart[256];    // first LDS slot of digit d
+  __shared__ uint32_t wcnt[4][256];   // per-wave digit counts, then per-wave offsets
   __shared__ uint32_t tmp[4];
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
+  const int64_t blk = blockIdx.x;
 
+  // this tile's count of digit t, from the scanned (exclusive) histogram row
+  const uint32_t h0 = hist[(int64_t)t * nblk + blk];
+  const uint32_t h1 = blk + 1 < nblk ? hist[(int64_t)t * nblk + blk + 1] : dtot[t];
   uint32_t tot;
   const uint32_t dpre = block_exclusive_scan_256(dtot[t], tmp, &tot);
-  dbase[t] = dpre + hist[(int64_t)t * nblk + blockIdx.x];
-  running[t] = 0;
+  const uint32_t ls = block_exclusive_scan_256(h1 - h0, tmp, &tot);
+  lstart[t] = ls;
+  gbase[t] = dpre + h0 - ls;
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) wc[q][ww][t] = 0;
+  for (int ww = 0; ww < 4; ++ww) wcnt[ww][t] = 0;
   __syncthreads();
 
-  const int64_t base = (int64_t)blockIdx.x * kSortTile;
-  for (int r = 0; r < kIPT; ++r) {
-    const int64_t i = base + r * kT + t;
+  const int64_t base = blk * kSortTile + (int64_t)w * KW;
+  uint32_t kr[RW], vr[RW], rr[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int64_t i = base + r * 64 + lane;
     const bool valid = i < n;
-    const uint32_t k = valid ? key(i) : 0u;
-    const uint32_t v = valid ? (vals_in ? vals_in[i] : (uint32_t)i) : 0u;
-    const uint32_t d = (k >> shift) & 255u;
+    kr[r] = valid ? key(i) : 0u;
+    vr[r] = valid ? (vals_in ? vals_in[i] : (uint32_t)i) : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int64_t i = base + r * 64 + lane;
+    const bool valid = i < n;
+    const uint32_t d = (kr[r] >> shift) & 255u;
     const uint64_t m = match_digit(d, valid);
     const uint32_t lrank = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-    const uint32_t tag = (uint32_t)(r + 1) << 16;
-    uint32_t(*wr)[256] = wc[r & 1];
-    if (valid && lrank == 0) wr[w][d] = (uint32_t)__popcll(m) | tag;
-    __syncthreads();
-    if (valid) {
-      uint32_t pre = 0;
-      for (int ww = 0; ww < w; ++ww) {
-        const uint32_t c = wr[ww][d];
-        if ((c & 0xFFFF0000u) == tag) pre += c & 0xFFFFu;
-      }
-      const uint32_t pos = dbase[d] + running[d] + pre + lrank;
-      keys_out[pos] = k;
-      vals_out[pos] = v;
-    }
-    __syncthreads();
-    uint32_t add = 0;
+    const uint32_t before = wcnt[w][d];
+    rr[r] = before + lrank;
+    if (valid && lrank == 0) wcnt[w][d] = before + (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  {  // per-wave counts -> exclusive per-wave offsets (thread t owns digit t)
+    uint32_t run = 0;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const uint32_t c = wr[ww][t];
-      if ((c & 0xFFFF0000u) == tag) add += c & 0xFFFFu;
+      const uint32_t c = wcnt[ww][t];
+      wcnt[ww][t] = run;
+      run += c;
     }
-    running[t] += add;
-    // the next round's first barrier orders this update before its reads
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int64_t i = base + r * 64 + lane;
+    if (i < n) {
+      const uint32_t d = (kr[r] >> shift) & 255u;
+      const uint32_t slot = lstart[d] + wcnt[w][d] + rr[r];
+      lkey[slot] = kr[r];
+      lval[slot] = vr[r];
+    }
+  }
+  __syncthreads();
+  const int64_t rem = n - blk * kSortTile;
+  const int cnt = rem < kSortTile ? (int)rem : kSortTile;
+  for (int i = t; i < cnt; i += kT) {
+    const uint32_t k = lkey[i];
+    const uint32_t pos = gbase[(k >> shift) & 255u] + (uint32_t)i;
+    keys_out[pos] = k;
+    vals_out[pos] = lval[i];
   }
 }
 
+// off[k] for every k in [0, nseg]: row i writes the offsets of the keys in
+// (key[i-1], key[i]]; the last row also closes (key[n-1], nseg].  Keys that
+// no row carries are empty clusters: when `counts` is given they get count 0
+// and keep their previous centroid (C_new[k] = C_prev[k]).
 __global__ __launch_bounds__(kT) void segment_offsets_kernel(const uint32_t* __restrict__ keys, int64_t n,
-                                                             uint32_t nseg, int32_t* __restrict__ off) {
+                                                             uint32_t nseg, int32_t* __restrict__ off,
+                                                             EmptyOut eo) {
   const int64_t i = (int64_t)blockIdx.x * kT + threadIdx.x;
   if (i >= n) return;
   const int64_t k = keys[i] < nseg ? (int64_t)keys[i] : (int64_t)nseg;
   const int64_t kp = i == 0 ? -1 : (keys[i - 1] < nseg ? (int64_t)keys[i - 1] : (int64_t)nseg);
   for (int64_t kk = kp + 1; kk <= k; ++kk) off[kk] = (int32_t)i;
-  if (i == n - 1)
+  auto empty = [&](int64_t kk) {
+    eo.counts[kk] = 0;
+    if (eo.C_new != eo.C_prev) {  // D is a multiple of 4: copy the row as float4
+      const float4* src = reinterpret_cast<const float4*>(eo.C_prev + kk * eo.D);
+      float4* dst = reinterpret_cast<float4*>(eo.C_new + kk * eo.D);
+#pragma unroll 8
+      for (int d = 0; d < eo.D / 4; ++d) dst[d] = src[d];
+    }
+  };
+  if (eo.counts)
+    for (int64_t kk = kp + 1; kk < k; ++kk) empty(kk);
+  if (i == n - 1) {
     for (int64_t kk = k + 1; kk <= (int64_t)nseg; ++kk) off[kk] = (int32_t)n;
+    if (eo.counts)
+      for (int64_t kk = k + 1; kk < (int64_t)nseg; ++kk) empty(kk);
+  }
 }
 
 template <class KeyFn>
@@ -217,9 +269,9 @@ hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K,
 }
 
 hipError_t launch_segment_offsets(const uint32_t* sorted_keys, int64_t n, uint32_t nseg, int32_t* off,
-                                  hipStream_t s) {
+                                  const EmptyOut& eo, hipStream_t s) {
   const int64_t grid = (n + kT - 1) / kT;
-  segment_offsets_kernel<<<dim3((unsigned)grid), dim3(kT), 0, s>>>(sorted_keys, n, nseg, off);
+  segment_offsets_kernel<<<dim3((unsigned)grid), dim3(kT), 0, s>>>(sorted_keys, n, nseg, off, eo);
   return hipGetLastError();
 }
 

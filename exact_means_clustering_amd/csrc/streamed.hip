@@ -148,7 +148,8 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
       const uint32_t* skeys = nullptr;
       const uint32_t* perm = nullptr;
       KS_HIP(launch_argsort_labels(lslot[sl], rows, 1, K, w.sort, &skeys, &perm, r.cs), "argsort launch");
-      KS_HIP(launch_segment_offsets(skeys, rows, (uint32_t)K, w.off, r.cs), "segment offsets launch");
+      KS_HIP(launch_segment_offsets(skeys, rows, (uint32_t)K, w.off, EmptyOut{nullptr, nullptr, nullptr, D}, r.cs),
+             "segment offsets launch");
       SegOut so{nullptr, nullptr, nullptr, S_acc, n_acc};
       KS_HIP(launch_segment_reduce(dtype, D, xslot[sl], perm, skeys, w.off, rows, (uint32_t)K, so, w.seg, r.cs),
              "segment reduce launch");
