@@ -40,8 +40,8 @@ def parse():
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="rows in the oracle timing sample")
-    ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON file with measured HBM bytes per assign launch (from rocprofv3 counters)")
+    ap.add_argument("--probe", action="store_true",
+                    help="counter-collection target: one 1 GiB device copy (calibration) and one step, no timing")
     return ap.parse_args()
 
 
@@ -74,6 +74,68 @@ def cpu_baseline(p, sample_rows):
                        f"linearly by N/{rows:,}")}
 
 
+ASSIGN_SOURCES = ["exact_means_clustering_amd/csrc/assign.hip", "exact_means_clustering_amd/csrc/common.h"]
+
+
+def assign_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ASSIGN_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def assign_traffic(name, B, N, D, K):
+    """HBM bytes per assign launch from the committed counter summary
+    profiles/traffic_<workload>.txt, or None if absent, for another shape, or
+    taken on a different assign kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        if kv.get("assign_source_sha256") != assign_source_sha():
+            return None
+        if (int(kv["B"]), int(kv["N"]), int(kv["D"]), int(kv["K"])) != (B, N, D, K):
+            return None
+        fetch_factor = float(kv["copy_bytes"]) / (float(kv["copy_fetch_kib"]) * 1024)
+        write_factor = float(kv["copy_bytes"]) / (float(kv["copy_write_kib"]) * 1024)
+        return (float(kv["assign_fetch_kib"]) * 1024 * fetch_factor
+                + float(kv["assign_write_kib"]) * 1024 * write_factor)
+    except (KeyError, ValueError):
+        return None
+
+
+def probe(args):
+    """Counter-collection target: a plain 1 GiB device copy (calibrates
+    FETCH_SIZE / WRITE_SIZE) followed by one assign and one update."""
+    import torch
+
+    import datagen
+    import exact_means_clustering_amd as km
+
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    p = datagen.make(args.config, n=args.n, k=args.k)
+    X = (p.X if p.B > 1 else p.X[0]).cuda()
+    C = (p.C0 if p.B > 1 else p.C0[0]).cuda()
+    ws = torch.empty(km.workspace_bytes(p.N, p.D, p.K, p.B, X.dtype), dtype=torch.uint8, device="cuda")
+    labels, _, _ = km.assign(X, C, ws=ws)
+    km.update(X, labels, C, ws=ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": args.config, "B": p.B, "N": p.N, "D": p.D, "K": p.K,
+                      "assign_source_sha256": assign_source_sha()}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -89,6 +151,8 @@ def main():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         sys.exit(2)
     name = args.config
+    if args.probe:
+        return probe(args)
     if name == "c5":
         return bench_streamed(args)
     t0 = time.time()
@@ -142,9 +206,7 @@ def main():
     upd_bytes = B * (N * D * sz + 4 * N + 4 * K * D + 4 * K)
     u_gbs = upd_bytes / (u_ms * 1e-3) / 1e9
     peak = PEAK_TFLOPS[p.dtype]
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get(name)
+    traffic = assign_traffic(name, B, N, D, K)
     out = {
         "metric": METRIC,
         "value": 1000.0 / ms_step,
@@ -168,9 +230,12 @@ def main():
         "update_frac_hbm_peak": u_gbs / PEAK_HBM_GBS,
         "roofline": {"bound": "mfma", "achieved": a_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": a_tflops / peak, "traffic": traffic},
+        "roofline_update": {"bound": "hbm", "achieved": u_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": u_gbs / PEAK_HBM_GBS, "algorithmic_bytes": upd_bytes},
     }
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or {"c1": 65536, "c2": 65536, "c3": 16384, "c4": 4096}[name]
+        # rows of the oracle's timing sample: about 10-30 s of host work each
+        sample = args.cpu_sample or {"c1": 65536, "c2": 1 << 20, "c3": 1 << 17, "c4": 16384}[name]
         out["cpu_baseline"] = cpu_baseline(p, sample)
     print(json.dumps(out), flush=True)
 

@@ -312,3 +312,27 @@ def pin_libraries(L):
 
 ALL_PINS = [pin_rounding, pin_decode, pin_bruteforce, pin_closed_forms, pin_planted, pin_invariants,
             pin_libraries]
+
+
+# ------------------------------------------------------ comparison helpers
+
+
+def pin_helpers(L):
+    """near_tie_report and centroid_rel_err against hand-computed cases."""
+    X = np.array([[1.0, 0.0], [0.0, 2.0], [3.0, 3.0]])
+    C = np.array([[1.0, 0.0], [1.0 + 1e-7, 0.0], [0.0, 2.0], [5.0, 5.0]])
+    # row 0: centroids 0 and 1 are a near-tie (gap 1e-14 << 1e-5 * ||x||^2 = 1e-5)
+    # row 1: candidate picks 3 (far): a real failure; row 2: exact
+    rep = L.near_tie_report(X, C, np.array([1, 3, 3]), np.array([0, 2, 3]))
+    assert rep["mismatch"] == 2 and rep["excused"] == 1 and rep["failed"] == 1 and rep["fail_rows"] == [1]
+    rep = L.near_tie_report(X, C, np.array([0, 2, 3]), np.array([0, 2, 3]))
+    assert rep["mismatch"] == 0 and rep["failed"] == 0
+    # x = 0: the tolerance is zero, so even an exact tie is not excused
+    rep = L.near_tie_report(np.zeros((1, 2)), np.array([[1.0, 0.0], [-1.0, 0.0]]), np.array([1]), np.array([0]))
+    assert rep["failed"] == 1
+    # centroid error: ||(3,4) - (0,0)|| / max(||(0,0)||, 1e-3 * 2000) = 5 / 2
+    assert abs(L.centroid_rel_err([[3.0, 4.0], [1.0, 1.0]], [[0.0, 0.0], [1.0, 1.0]], 2000.0) - 2.5) < 1e-15
+    assert abs(L.centroid_rel_err([[1.0, 1.0 + 1e-3]], [[1.0, 1.0]], 1.0) - 1e-3 / np.sqrt(2)) < 1e-15
+
+
+ALL_PINS.append(pin_helpers)
