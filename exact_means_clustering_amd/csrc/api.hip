@@ -3,7 +3,7 @@
 #include "kernels.h"
 #include "workspace.h"
 
-#include "../../include/flashkm.h"
+#include "flashkm.h"
 
 using namespace fkm;
 
@@ -41,7 +41,7 @@ int check_ws(const void* ws, size_t ws_bytes, const Layout& L) {
 // prep + assign (+ inertia) on stream s
 int run_assign(const void* X, int dt, int64_t N, int D, int B, const float* C, int K, int32_t* labels,
                float* min_d2, double* inertia, double* hist, Work& w, hipStream_t s) {
-  KM_HIP(launch_prep(dt, D, C, w.chat, w.hb, (int64_t)B * K, s), "centroid prep launch");
+  KM_HIP(launch_prep(dt, D, C, w.chat, w.hb, B, K, s), "centroid prep launch");
   const AssignConfig cfg = assign_pick(dt, D, N, B);
   KM_HIP(launch_assign(dt, D, cfg, X, w.chat, w.hb, N, K, B, labels, min_d2, w.part, s), "assign launch");
   if (inertia) {

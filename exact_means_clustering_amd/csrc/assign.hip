@@ -21,10 +21,10 @@
 // single contiguous loads and stay in registers for the whole sweep, and
 // centroid fragments are contiguous 16-byte LDS reads.
 //
-// Pipeline.  Centroids stream through a double-buffered LDS tile of 64 rows
-// (16-byte chunks XOR-swizzled by row so a 32-row fragment read is free of
-// bank conflicts); the global loads of tile t+1 are issued before the MFMAs
-// of tile t.  One barrier per tile.
+// Pipeline.  Centroids stream through a double-buffered LDS tile (16-byte
+// chunks XOR-swizzled by row so a 32-row fragment read is free of bank
+// conflicts), loaded straight from global memory into LDS; the loads of
+// tile t+1 are issued before the MFMAs of tile t.  One barrier per tile.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,12 +37,21 @@ namespace fkm {
 // ---------------------------------------------------------------------------
 // centroid preparation: Chat = RNE(C -> dtype), hb = -0.5 ||Chat||^2 (fp32)
 // ---------------------------------------------------------------------------
+// One wave per slot of the padded bias array [B][Kp]: slots k < K prepare
+// centroid k of their instance, slots k >= K hold -inf (never chosen).
 template <class T, int D>
 __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, typename T::raw* __restrict__ Ch,
-                                                   float* __restrict__ hb, int64_t rows) {
+                                                   float* __restrict__ hb, int64_t B, int K, int Kp) {
   const int lane = lane_id();
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int64_t slot = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (slot >= B * Kp) return;
+  const int64_t b = slot / Kp;
+  const int k = (int)(slot - b * Kp);
+  if (k >= K) {
+    if (lane == 0) hb[slot] = -INFINITY;
+    return;
+  }
+  const int64_t row = b * K + k;
   constexpr int PER = (D + kWave - 1) / kWave;
   float ss = 0.f;
 #pragma unroll
@@ -56,7 +65,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, 
     }
   }
   ss = wave_sum_f32(ss);
-  if (lane == 0) hb[row] = -0.5f * ss;
+  if (lane == 0) hb[slot] = -0.5f * ss;
 }
 
 // ---------------------------------------------------------------------------
@@ -66,7 +75,9 @@ template <class T, int D, int PB, int W>
 struct AssignCfg {
   static constexpr int RB = D * T::SZ;                 // bytes per row
 #ifndef FKM_TK
-  static constexpr int TK = RB <= 256 ? 128 : 64;      // centroids per LDS tile
+  // centroids per LDS tile: 256 for 8-wave workgroups (one per CU, fewer
+  // barriers), 128 otherwise; 64 for rows over 256 bytes
+  static constexpr int TK = RB <= 256 ? (W == 8 ? 256 : 128) : 64;
 #else
   static constexpr int TK = RB <= 256 ? FKM_TK : 64;
 #endif
@@ -90,9 +101,11 @@ struct AssignCfg {
   static constexpr int STEPS = (D / 2) / T::KPL;       // MFMA steps per 32x32 tile
   static constexpr int TILE_CH = TK * NCH;             // chunks per LDS tile
   static constexpr int THREADS = W * 64;
-  static constexpr int PRE = (TILE_CH + THREADS - 1) / THREADS;  // chunks per thread per tile load
+  static constexpr int DMA_INSTS = TILE_CH / 64;                  // 64-lane LDS loads per tile
+  static constexpr int DMA_PER_WAVE = (DMA_INSTS + W - 1) / W;    // per wave (upper bound)
   static constexpr int ROWS = W * 32 * PB;                       // points per workgroup
   static_assert(NCH >= 2 && (NCH & (NCH - 1)) == 0, "row must be a power-of-two number of 16B chunks");
+  static_assert(TILE_CH % 64 == 0 && TK % 4 == 0 && TK / 4 <= 64, "tile must be whole 64-lane LDS loads");
 };
 
 __device__ __forceinline__ float max16(const f32x16& a) {
@@ -127,7 +140,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
                                                         int32_t* __restrict__ labels, float* __restrict__ min_d2,
                                                         double* __restrict__ part) {
   using Cfg = AssignCfg<T, D, PB, W>;
-  constexpr int NCH = Cfg::NCH, HV = Cfg::HV, STEPS = Cfg::STEPS, PRE = Cfg::PRE, NT = Cfg::THREADS;
+  constexpr int NCH = Cfg::NCH, HV = Cfg::HV, STEPS = Cfg::STEPS;
   constexpr int TK = Cfg::TK;
   __shared__ uint4 tile[2][Cfg::TILE_CH];
   __shared__ __align__(16) float tb[2][TK];  // read back as float4
@@ -147,7 +160,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
     const int64_t blk = job - (int64_t)b * nblk;
     const typename T::raw* Xb = X + (int64_t)b * N * D;
     const typename T::raw* Cb = Ch + (int64_t)b * K * D;
-    const float* hbb = hb + (int64_t)b * K;
+    const float* hbb = hb + (int64_t)b * kpad(K);
     const int64_t p0 = blk * Cfg::ROWS + (int64_t)w * (PB * 32);
 
     // point fragments: lane half h holds dims [h*D/2, (h+1)*D/2) of point col
@@ -161,34 +174,34 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
       for (int v = 0; v < HV; ++v) xf[p][v] = src[v];
     }
 
-    uint4 pre[PRE];
-    float preb = 0.f;
-    auto load_tile = [&](int t) {
+    // Tile t goes straight from global memory into LDS buffer `buf`
+    // (global_load_lds: lane l of a wave writes 16 bytes at the instruction's
+    // LDS base + 16*l), so nothing is staged in registers.  The XOR swizzle is
+    // applied on the global side: LDS chunk q of the tile (row m = q / NCH,
+    // physical chunk q % NCH) receives logical chunk (q % NCH) ^ (m % NCH) of
+    // centroid row m.  Rows past K read row K-1 (their bias is -inf).  The
+    // bias slice comes from the -inf-padded array in 16-byte pieces.
+    auto issue_tile = [&](int t, int buf) {
 #pragma unroll
-      for (int i = 0; i < PRE; ++i) {
-        const int q = tid + NT * i;
-        if (q < Cfg::TILE_CH) {
-          const int m = q / NCH, c = q % NCH;
-          const int k = t * TK + m;
-          pre[i] = k < K ? reinterpret_cast<const uint4*>(Cb + (int64_t)k * D)[c] : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < Cfg::DMA_PER_WAVE; ++i) {
+        const int ins = i * W + w;  // wave-uniform instruction index within the tile
+        if (ins < Cfg::DMA_INSTS) {
+          const int q = ins * 64 + lane;
+          const int m = q / NCH, pc = q % NCH;
+          int k = t * TK + m;
+          k = k < K ? k : K - 1;
+          const uint4* src = reinterpret_cast<const uint4*>(Cb + (int64_t)k * D) + (pc ^ (m & (NCH - 1)));
+          __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&tile[buf][ins * 64], 16,
+                                           0, 0);
         }
       }
-      if (tid < TK) {
-        const int k = t * TK + tid;
-        preb = k < K ? hbb[k] : -INFINITY;
+      if (w == W - 1 && lane < TK / 4) {
+        const float4* src = reinterpret_cast<const float4*>(hbb + (int64_t)t * TK) + lane;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&tb[buf][0], 16, 0, 0);
       }
     };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < PRE; ++i) {
-        const int q = tid + NT * i;
-        if (q < Cfg::TILE_CH) {
-          const int m = q / NCH, c = q % NCH;
-          tile[buf][m * NCH + (c ^ (m & (NCH - 1)))] = pre[i];
-        }
-      }
-      if (tid < TK) tb[buf][tid] = preb;
-    };
+    // all of this wave's LDS loads have landed (then a barrier publishes them)
+    auto wait_tile = [] { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ };
 
     float best[PB];
     int bidx[PB];
@@ -198,8 +211,8 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
       bidx[p] = 0;
     }
 
-    load_tile(0);
-    store_tile(0);
+    issue_tile(0, 0);
+    wait_tile();
     __syncthreads();
 
     // The centroid tile is consumed in groups of G sub-blocks of 32
@@ -261,7 +274,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
 
     for (int t = 0; t < ntiles; ++t) {
       const int buf = t & 1;
-      if (t + 1 < ntiles) load_tile(t + 1);
+      if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
       uint4 afn[G][HV];
       if constexpr (Cfg::APF) {
 #pragma unroll
@@ -269,6 +282,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
       }
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
+        if (t * TK + g * G * 32 >= K) break;  // the rest of the tile is -inf padding
         uint4 af[G][HV];
         if constexpr (Cfg::APF) {
 #pragma unroll
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
           reduce_group(acc, base);
         }
       }
-      if (t + 1 < ntiles) store_tile(buf ^ 1);
+      wait_tile();
       __syncthreads();
     }
     if constexpr (Cfg::DELAY) reduce_group(prev, prev_base);
@@ -394,11 +408,11 @@ __global__ __launch_bounds__(1024) void inertia_reduce_kernel(const double* __re
 namespace {
 
 template <class T, int D>
-hipError_t prep_t(const float* C, void* Chat, float* hb, int64_t rows, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  const int64_t grid = (rows + 3) / 4;
-  prep_kernel<T, D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(C, reinterpret_cast<typename T::raw*>(Chat), hb,
-                                                                rows);
+hipError_t prep_t(const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s) {
+  const int64_t slots = B * kpad(K);
+  const int64_t grid = (slots + 3) / 4;
+  prep_kernel<T, D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(C, reinterpret_cast<typename T::raw*>(Chat), hb, B,
+                                                                K, (int)kpad(K));
   return hipGetLastError();
 }
 
@@ -430,9 +444,12 @@ hipError_t assign_t(const void* X, const void* Chat, const float* hb, int64_t N,
 
 // Compiled configurations.  The point fragments of PB blocks take
 // PB * D * SZ / 8 VGPRs per lane, so deep blocking is limited to short rows.
+// (8-wave workgroups run two waves per SIMD, i.e. 256 registers per wave.)
 constexpr bool cfg_compiled(int row_bytes, int pb, int waves) {
-  if (pb == 1 && (waves == 4 || waves == 8)) return true;
-  if (pb == 2 && (waves == 4 || waves == 8)) return row_bytes <= 512;
+  if (pb == 1 && waves == 4) return true;
+  if (pb == 1 && waves == 8) return row_bytes <= 512;
+  if (pb == 2 && waves == 4) return row_bytes <= 512;
+  if (pb == 2 && waves == 8) return row_bytes <= 256;
   if (pb == 4 && waves == 4) return row_bytes <= 256;
   return false;
 }
@@ -477,8 +494,8 @@ hipError_t dispatch_dt_d(int dt, int D, A&&... a) {
 }
 
 template <class T, int D> struct PrepF {
-  static hipError_t run(const float* C, void* Chat, float* hb, int64_t rows, hipStream_t s) {
-    return prep_t<T, D>(C, Chat, hb, rows, s);
+  static hipError_t run(const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s) {
+    return prep_t<T, D>(C, Chat, hb, B, K, s);
   }
 };
 template <class T, int D> struct AssignF {
@@ -521,8 +538,8 @@ AssignConfig assign_pick(int dt, int D, int64_t N, int B) {
   return AssignConfig{1, 4};
 }
 
-hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t rows, hipStream_t s) {
-  return dispatch_dt_d<PrepF>(dt, D, C, Chat, hb, rows, s);
+hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s) {
+  return dispatch_dt_d<PrepF>(dt, D, C, Chat, hb, B, K, s);
 }
 
 hipError_t launch_assign(int dt, int D, AssignConfig cfg, const void* X, const void* Chat, const float* hb, int64_t N,

@@ -28,8 +28,11 @@ AssignConfig assign_pick(int dt, int D, int64_t N, int B);
 // Largest number of assign workgroups per instance over every configuration.
 inline int64_t assign_max_wgs(int64_t N) { return (N + 127) / 128; }
 
-// Chat[r] = RNE(C[r] -> dtype), hb[r] = -0.5 * ||Chat[r]||^2 for r < rows.
-hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t rows, hipStream_t s);
+// Centroid count padded for the bias array: a multiple of every assign tile.
+__host__ __device__ inline int64_t kpad(int K) { return ((int64_t)K + 255) / 256 * 256; }
+// Chat[b,k] = RNE(C[b,k] -> dtype) and hb[b * kpad(K) + k] = -0.5 * ||Chat[b,k]||^2
+// for k < K; hb[b * kpad(K) + k] = -inf for K <= k < kpad(K).
+hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s);
 
 // Fused distance + running argmin.  part[b * nwg + wg] receives each
 // workgroup's fp64 sum of min_d2 (nwg = ceil(N / rows_per_wg(pb))).

@@ -12,7 +12,7 @@
 #include "kernels.h"
 #include "workspace.h"
 
-#include "../../include/flashkm.h"
+#include "flashkm.h"
 
 using namespace fkm;
 
@@ -118,7 +118,7 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
 
   for (int t = 0; t < iters; ++t) {
     const float* Cs = t == 0 ? C0 : C_out;
-    KS_HIP(launch_prep(dtype, D, Cs, w.chat, w.hb, K, r.cs), "centroid prep launch");
+    KS_HIP(launch_prep(dtype, D, Cs, w.chat, w.hb, 1, K, r.cs), "centroid prep launch");
     KS_HIP(launch_zero_bytes(S_acc, (size_t)K * D * 8, r.cs), "zero launch");
     KS_HIP(launch_zero_bytes(n_acc, (size_t)K * 8, r.cs), "zero launch");
     KS_HIP(launch_zero_bytes(J_dev + t, 8, r.cs), "zero launch");

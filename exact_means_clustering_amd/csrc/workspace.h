@@ -35,7 +35,7 @@ inline Layout make_layout(int64_t N, int D, int K, int B, int dt) {
   const int64_t nseg = (int64_t)B * K;
   size_t o = 0;
   L.chat = o;  o = al256(o + (size_t)nseg * D * dtype_size(dt));
-  L.hb = o;    o = al256(o + (size_t)nseg * 4);
+  L.hb = o;    o = al256(o + (size_t)B * kpad(K) * 4);
   L.part = o;  o = al256(o + (size_t)B * assign_max_wgs(N) * 8);
   L.cnt = o;   o = al256(o + (size_t)nseg * 4);
   L.keys0 = o; o = al256(o + (size_t)n * 4);
