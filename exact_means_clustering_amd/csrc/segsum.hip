@@ -190,9 +190,9 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
 // ---------------------------------------------------------------------------
 // level 2: per group of chunks, combine chunk fragments (fp64)
 // ---------------------------------------------------------------------------
-// One wave per group.  The group's segments are scanned 64 at a time (one
-// coalesced load of their offsets); a ballot picks the ones that cross a
-// chunk edge, and only those are summed.
+// One workgroup of 4 waves per group.  The group's segments are scanned 64
+// at a time (one coalesced load of their offsets); a ballot picks the ones
+// that cross a chunk edge, and those are dealt round-robin to the 4 waves.
 template <int D>
 __global__ __launch_bounds__(256) void seg_level2_kernel(const uint32_t* __restrict__ keys,
                                                          const int32_t* __restrict__ off, int64_t n, SegOut o,
@@ -201,18 +201,24 @@ __global__ __launch_bounds__(256) void seg_level2_kernel(const uint32_t* __restr
   constexpr int64_t U = kSegRows;
   constexpr int64_t UG = (int64_t)kSegRows * kSegGroup;
   const int lane = lane_id();
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int w = threadIdx.x >> 6;
+  const int64_t g = blockIdx.x;
   const int64_t gr0 = g * UG;
   if (gr0 >= n) return;
   const int64_t gr1 = gr0 + UG < n ? gr0 + UG : n;
   const int64_t kf = keys[gr0], kl = keys[gr1 - 1];
+  int turn = 0;  // crossing segments seen so far in this group
   for (int64_t k0 = kf; k0 <= kl; k0 += 64) {
     const int64_t kk = k0 + lane;
     const bool valid = kk <= kl;
     const int64_t sv = valid ? off[kk] : 0, ev = valid ? off[kk + 1] : 0;
     // crosses a chunk edge (a segment inside one chunk was finished at level 1)
     const bool cross = valid && sv < ev && (sv / U != (ev - 1) / U);
-    uint64_t mask = __ballot(cross);
+    uint64_t all = __ballot(cross);
+    // this wave's share: every 4th crossing segment in order
+    uint64_t mask = 0;
+    for (uint64_t m = all; m; m &= m - 1, ++turn)
+      if ((turn & 3) == w) mask |= m & (~m + 1);
     while (mask) {
       const int j = __ffsll((unsigned long long)mask) - 1;
       mask &= mask - 1;
@@ -252,8 +258,9 @@ __global__ __launch_bounds__(256) void seg_level2_kernel(const uint32_t* __restr
 // ---------------------------------------------------------------------------
 // A segment crossing into group g from the left and ending in it is owned by
 // g.  One workgroup of kL3Waves waves covers kL3Waves groups: each wave checks
-// its group's ownership, then all waves sum each owned segment's group
-// fragments together (interleaved by wave, combined in wave order).
+// its group's ownership and finishes an owned segment spanning at most
+// kL3Waves groups by itself; longer segments are then summed by all waves
+// together (interleaved by wave, combined in wave order).
 constexpr int kL3Waves = 16;
 template <int D>
 __global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint32_t* __restrict__ keys,
@@ -266,7 +273,7 @@ __global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint32_
   __shared__ int64_t own_k[kL3Waves], own_s[kL3Waves], own_e[kL3Waves];
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
-  if (lane == 0) {
+  {
     const int64_t g = (int64_t)blockIdx.x * kL3Waves + w;
     int64_t k = -1, s = 0, e = 0;
     if (g < ngroups) {
@@ -277,14 +284,33 @@ __global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint32_
       e = off[kk + 1];
       if (s < gr0 && e <= gr1) k = kk;
     }
-    own_k[w] = k;
-    own_s[w] = s;
-    own_e[w] = e;
+    if (k >= 0 && g - s / UG < kL3Waves) {
+      // short span: this wave alone, in group order
+      double acc[PER];
+#pragma unroll
+      for (int q = 0; q < PER; ++q) acc[q] = 0.0;
+#pragma unroll 4
+      for (int64_t gg = s / UG; gg <= g; ++gg) {
+        const double* gp = gfrag + (gg * 2 + frag_slot(gg, UG, s)) * D;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int d = lane + 64 * q;
+          if (d < D) acc[q] += gp[d];
+        }
+      }
+      finish<PER>(o, k, D, lane, acc, e - s);
+      k = -1;
+    }
+    if (lane == 0) {
+      own_k[w] = k;
+      own_s[w] = s;
+      own_e[w] = e;
+    }
   }
   __syncthreads();
   for (int ow = 0; ow < kL3Waves; ++ow) {
     const int64_t k = own_k[ow];
-    if (k < 0) continue;  // uniform over the workgroup
+    if (k < 0) continue;  // uniform over the workgroup: long segments only
     const int64_t s = own_s[ow], e = own_e[ow];
     const int64_t g_end = (int64_t)blockIdx.x * kL3Waves + ow;
     double acc[PER];
@@ -342,8 +368,7 @@ hipError_t seg_reduce_t(const void* X, const uint32_t* perm, const uint32_t* key
   seg_level1_kernel<T, D><<<dim3((unsigned)((nchunks + 3) / 4)), dim3(256), 0, s>>>(
       reinterpret_cast<const typename T::raw*>(X), perm, keys, n, o, buf.frag);
   if (nchunks > 1) {
-    seg_level2_kernel<D><<<dim3((unsigned)((ngroups + 3) / 4)), dim3(256), 0, s>>>(keys, off, n, o, buf.frag,
-                                                                                  buf.gfrag);
+    seg_level2_kernel<D><<<dim3((unsigned)ngroups), dim3(256), 0, s>>>(keys, off, n, o, buf.frag, buf.gfrag);
     if (ngroups > 1)
       seg_level3_kernel<D><<<dim3((unsigned)((ngroups + kL3Waves - 1) / kL3Waves)), dim3(kL3Waves * 64), 0, s>>>(
           keys, off, n, ngroups, o, buf.gfrag);

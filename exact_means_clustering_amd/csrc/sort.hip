@@ -210,11 +210,19 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(KeyFn key, const uint
 __global__ __launch_bounds__(kT) void segment_offsets_kernel(const uint32_t* __restrict__ keys, int64_t n,
                                                              uint32_t nseg, int32_t* __restrict__ off,
                                                              EmptyOut eo) {
-  const int64_t i = (int64_t)blockIdx.x * kT + threadIdx.x;
-  if (i >= n) return;
-  const int64_t k = keys[i] < nseg ? (int64_t)keys[i] : (int64_t)nseg;
-  const int64_t kp = i == 0 ? -1 : (keys[i - 1] < nseg ? (int64_t)keys[i - 1] : (int64_t)nseg);
-  for (int64_t kk = kp + 1; kk <= k; ++kk) off[kk] = (int32_t)i;
+  // four consecutive rows per thread (one 16-byte key load; the buffer is
+  // 256-byte aligned and i0 is a multiple of 4)
+  const int64_t i0 = ((int64_t)blockIdx.x * kT + threadIdx.x) * 4;
+  if (i0 >= n) return;
+  auto clampk = [&](uint32_t v) -> int64_t { return v < nseg ? (int64_t)v : (int64_t)nseg; };
+  uint32_t kv[4];
+  if (i0 + 3 < n) {
+    const uint4 q = *reinterpret_cast<const uint4*>(keys + i0);
+    kv[0] = q.x, kv[1] = q.y, kv[2] = q.z, kv[3] = q.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kv[j] = i0 + j < n ? keys[i0 + j] : 0u;
+  }
   auto empty = [&](int64_t kk) {
     eo.counts[kk] = 0;
     if (eo.C_new != eo.C_prev) {  // D is a multiple of 4: copy the row as float4
@@ -224,12 +232,21 @@ __global__ __launch_bounds__(kT) void segment_offsets_kernel(const uint32_t* __r
       for (int d = 0; d < eo.D / 4; ++d) dst[d] = src[d];
     }
   };
-  if (eo.counts)
-    for (int64_t kk = kp + 1; kk < k; ++kk) empty(kk);
-  if (i == n - 1) {
-    for (int64_t kk = k + 1; kk <= (int64_t)nseg; ++kk) off[kk] = (int32_t)n;
+  int64_t kp = i0 == 0 ? -1 : clampk(keys[i0 - 1]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = i0 + j;
+    if (i >= n) break;
+    const int64_t k = clampk(kv[j]);
+    for (int64_t kk = kp + 1; kk <= k; ++kk) off[kk] = (int32_t)i;
     if (eo.counts)
-      for (int64_t kk = k + 1; kk < (int64_t)nseg; ++kk) empty(kk);
+      for (int64_t kk = kp + 1; kk < k; ++kk) empty(kk);
+    if (i == n - 1) {
+      for (int64_t kk = k + 1; kk <= (int64_t)nseg; ++kk) off[kk] = (int32_t)n;
+      if (eo.counts)
+        for (int64_t kk = k + 1; kk < (int64_t)nseg; ++kk) empty(kk);
+    }
+    kp = k;
   }
 }
 
@@ -270,7 +287,7 @@ hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K,
 
 hipError_t launch_segment_offsets(const uint32_t* sorted_keys, int64_t n, uint32_t nseg, int32_t* off,
                                   const EmptyOut& eo, hipStream_t s) {
-  const int64_t grid = (n + kT - 1) / kT;
+  const int64_t grid = (n + 4 * kT - 1) / (4 * kT);
   segment_offsets_kernel<<<dim3((unsigned)grid), dim3(kT), 0, s>>>(sorted_keys, n, nseg, off, eo);
   return hipGetLastError();
 }
