@@ -131,6 +131,27 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
+// 16-byte load marked non-temporal (data read once: streamed past the caches
+// instead of displacing reusable lines).
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Workgroups are dispatched to the chip's 8 XCDs (each with its own L2) in
+// round-robin order of their index.  xcd_tile maps workgroup b of n to a
+// tile so that the workgroups of one XCD take one contiguous range of tiles:
+// neighbouring tiles then share that XCD's L2 (partial cache lines written
+// by adjacent tiles merge there).  It is a bijection on [0, n) whatever the
+// dispatch really does; only locality depends on it.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n) {
+  constexpr int kXcd = 8;
+  const int64_t q = n / kXcd, r = n % kXcd;
+  const int64_t x = b % kXcd, i = b / kXcd;
+  return x * q + (x < r ? x : r) + i;
+}
+
 // Exclusive prefix sum over a 256-thread block (4 waves).  `tmp` must hold 4
 // words.  Returns the exclusive prefix of `v`; *total receives the block sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan_256(uint32_t v, uint32_t* tmp, uint32_t* total) {

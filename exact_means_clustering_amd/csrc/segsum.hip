@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
 
   auto load_step = [&](int i) -> uint4 {
     const int j = i * SL + q;
-    if (i < nsteps && j < cnt) return reinterpret_cast<const uint4*>(X + (int64_t)srow[w][j] * D)[g];
+    if (i < nsteps && j < cnt) return load_nt(reinterpret_cast<const uint4*>(X + (int64_t)srow[w][j] * D) + g);
     return make_uint4(0, 0, 0, 0);
   };
 

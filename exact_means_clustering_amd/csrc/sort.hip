@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(KeyFn key, int64_t n, in
   const int t = threadIdx.x;
   cnt[t] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kSortTile;
+  const int64_t tile = xcd_tile(blockIdx.x, nblk);
+  const int64_t base = tile * kSortTile;
   uint32_t d[kIPT];
 #pragma unroll
   for (int r = 0; r < kIPT; ++r) {
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(KeyFn key, int64_t n, in
   for (int r = 0; r < kIPT; ++r)
     if (d[r] < 256u) atomicAdd(&cnt[d[r]], 1u);
   __syncthreads();
-  hist[(int64_t)t * nblk + blockIdx.x] = cnt[t];
+  hist[(int64_t)t * nblk + tile] = cnt[t];
 }
 
 // One workgroup per digit: exclusive scan of hist[d][0..nblk) in place,
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(KeyFn key, const uint
   __shared__ uint32_t tmp[4];
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
-  const int64_t blk = blockIdx.x;
+  const int64_t blk = xcd_tile(blockIdx.x, nblk);  // the tile this workgroup sorts
 
   // this tile's count of digit t, from the scanned (exclusive) histogram row
   const uint32_t h0 = hist[(int64_t)t * nblk + blk];
