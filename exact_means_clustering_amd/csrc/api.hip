@@ -51,18 +51,15 @@ int run_assign(const void* X, int dt, int64_t N, int D, int B, const float* C, i
   return KM_OK;
 }
 
-// argsort + offsets + segment means on stream s
+// argsort + segment offsets and means on stream s
 int run_update(const void* X, int dt, int64_t N, int D, int B, const int32_t* labels, int K, const float* C_prev,
                float* C_new, int32_t* counts, Work& w, hipStream_t s) {
-  const uint32_t* skeys = nullptr;
-  const uint32_t* perm = nullptr;
+  const uint2* sorted = nullptr;
   const int64_t n = N * B;
   const uint32_t nseg = (uint32_t)((int64_t)B * K);
-  KM_HIP(launch_argsort_labels(labels, N, B, K, w.sort, &skeys, &perm, s), "argsort launch");
+  KM_HIP(launch_argsort_labels(labels, N, B, K, w.sort, &sorted, s), "argsort launch");
   SegOut o{C_prev, C_new, counts ? counts : w.cnt, nullptr, nullptr};
-  const EmptyOut eo{C_prev, C_new, o.counts, D};
-  KM_HIP(launch_segment_offsets(skeys, n, nseg, w.off, eo, s), "segment offsets launch");
-  KM_HIP(launch_segment_reduce(dt, D, X, perm, skeys, w.off, n, nseg, o, w.seg, s), "segment reduce launch");
+  KM_HIP(launch_segment_reduce(dt, D, X, sorted, w.off, n, nseg, o, w.seg, s), "segment reduce launch");
   return KM_OK;
 }
 

@@ -44,31 +44,21 @@ hipError_t launch_assign(int dt, int D, AssignConfig cfg, const void* X, const v
 hipError_t launch_inertia_reduce(const double* part, int nwg, int B, double* inertia, double* hist,
                                  bool accumulate, hipStream_t s);
 
-// ---- inverse mapping (stable LSD radix argsort + segment offsets) -----------
+// ---- inverse mapping (stable LSD radix argsort) -------------------------------
 constexpr int kSortTile = 4096;  // keys per sort workgroup
 inline int64_t sort_blocks(int64_t n) { return (n + kSortTile - 1) / kSortTile; }
 
+// Sort elements are (key, row) pairs packed in one 8-byte word, so a pass
+// reads and writes each element with a single access.
 struct SortBuffers {
-  uint32_t* keys[2];
-  uint32_t* vals[2];
+  uint2* kv[2];     // [n] each: ping-pong pair buffers
   uint32_t* hist;   // [256 * nblk]
   uint32_t* dtot;   // [256]
 };
 // Sorts rows by key = b*K + clamp(labels[b*N+i], 0, K-1) (stable).  On return
-// *sorted_keys / *perm point at the buffers holding the result.
+// *sorted points at the buffer holding the sorted (key, row) pairs.
 hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K, SortBuffers& buf,
-                                 const uint32_t** sorted_keys, const uint32_t** perm, hipStream_t s);
-// Empty-cluster output of the offsets pass: when counts is non-null, every
-// key no row carries gets counts[k] = 0 and C_new[k] = C_prev[k] (D floats).
-struct EmptyOut {
-  const float* C_prev;
-  float* C_new;
-  int32_t* counts;
-  int D;
-};
-// off[k] = #{rows with key < k} for k in [0, nseg]
-hipError_t launch_segment_offsets(const uint32_t* sorted_keys, int64_t n, uint32_t nseg, int32_t* off,
-                                  const EmptyOut& eo, hipStream_t s);
+                                 const uint2** sorted, hipStream_t s);
 
 // ---- segment-local reductions ----------------------------------------------
 #ifndef FKM_SEG_ROWS
@@ -97,9 +87,9 @@ struct SegOut {
   double* S_acc;
   int64_t* n_acc;
 };
-hipError_t launch_segment_reduce(int dt, int D, const void* X, const uint32_t* perm, const uint32_t* sorted_keys,
-                                 const int32_t* off, int64_t n, uint32_t nseg, const SegOut& out,
-                                 SegBuffers& buf, hipStream_t s);
+// Also writes the segment offsets off[k] = #{rows with key < k}, k in [0, nseg].
+hipError_t launch_segment_reduce(int dt, int D, const void* X, const uint2* sorted, int32_t* off, int64_t n,
+                                 uint32_t nseg, const SegOut& out, SegBuffers& buf, hipStream_t s);
 
 // ---- streamed path helpers ---------------------------------------------------
 // C_new[k] = S[k] / n[k] (fp64 divide, rounded once to fp32) when n[k] > 0,

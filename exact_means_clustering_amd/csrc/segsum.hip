@@ -6,11 +6,14 @@
 // After the argsort, cluster k owns the contiguous sorted positions
 // [off[k], off[k+1]).  The sorted order is cut into fixed chunks of kSegRows
 // positions, one wave each:
-//   level 1  a wave sums, per segment piece inside its chunk, the gathered
-//            rows X[perm[j]] in fp32 (4 rows in flight per 64 lanes for
-//            D*SZ = 256 B).  A segment that lies inside the chunk is finished
-//            on the spot; the chunk's first / last piece of a segment that
-//            crosses the chunk edge goes to fragment slot 0 / 1.
+//   level 1  a wave writes the segment offsets off[k] of the segments that
+//            start in its chunk, then sums, per segment piece inside the
+//            chunk, the gathered rows X[perm[j]] in fp32 (4 rows per 64-lane
+//            load for D*SZ = 256 B).  A segment that lies inside the chunk is
+//            finished on the spot; the chunk's first / last piece of a
+//            segment that crosses the chunk edge goes to fragment slot 0 / 1.
+//            (Means mode: clusters no row carries are then filled from
+//            C_prev by a separate parallel pass.)
 //   level 2  one wave per group of kSegGroup chunks adds (fp64) the chunk
 //            fragments of every segment that crosses a chunk edge; segments
 //            inside the group are finished, the others leave group fragments.
@@ -73,8 +76,8 @@ constexpr int kRing = FKM_RING;
 
 template <class T, int D>
 __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* __restrict__ X,
-                                                         const uint32_t* __restrict__ perm,
-                                                         const uint32_t* __restrict__ keys, int64_t n, SegOut o,
+                                                         const uint2* __restrict__ kv, int64_t n, uint32_t nseg,
+                                                         int32_t* __restrict__ off, SegOut o,
                                                          float* __restrict__ frag) {
   constexpr int VEC = Vec<T>::N;           // elements per 16-byte word
   constexpr int LPR = D * T::SZ / 16;      // lanes per row
@@ -90,16 +93,18 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
   const bool active = r0 < n;
   const int cnt = active ? (int)(n - r0 < U ? n - r0 : U) : 0;
   for (int e = lane; e < U; e += 64) {
-    skey[w][e] = e < cnt ? keys[r0 + e] : 0xFFFFFFFFu;
-    srow[w][e] = e < cnt ? perm[r0 + e] : 0u;
+    const uint2 v = e < cnt ? kv[r0 + e] : make_uint2(0xFFFFFFFFu, 0u);
+    skey[w][e] = v.x;
+    srow[w][e] = v.y;
   }
   __syncthreads();
   if (!active) return;
   const int q = lane / LPR, g = lane % LPR;
   const uint32_t kf = skey[w][0], kl = skey[w][cnt - 1];
+  const int64_t kbefore = r0 > 0 ? (int64_t)kv[r0 - 1].x : -1;  // key of the row before the chunk
   // does the chunk's first (last) segment continue from the previous (into the next) chunk?
-  const bool cont_left = r0 > 0 && keys[r0 - 1] == kf;
-  const bool cont_right = r0 + cnt < n && keys[r0 + cnt] == kl;
+  const bool cont_left = kbefore == (int64_t)kf;
+  const bool cont_right = r0 + cnt < n && kv[r0 + cnt].x == kl;
   const int nsteps = (cnt + SL - 1) / SL;
 
   auto load_step = [&](int i) -> uint4 {
@@ -151,6 +156,41 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
   uint4 ring[kRing];
 #pragma unroll
   for (int u = 0; u < kRing; ++u) ring[u] = load_step(u);
+
+  // Segment offsets (while the first row loads are in flight).  A row whose
+  // key k differs from the previous row's key kp starts segment k:
+  // off[kk] = its position for every kk in (kp, k] (keys no row carries get
+  // the start of the next present key), and the last row of the order also
+  // sets off[kk] = n for kk in (k, nseg].  A lane fills a short range itself;
+  // ranges of 64 or more keys are filled by the whole wave, one coalesced
+  // store per 64 keys.
+  for (int e0 = 0; e0 < cnt; e0 += 64) {
+    const int e = e0 + lane;
+    int64_t a = 0, b = -1, a2 = 0, b2 = -1;
+    int32_t val = 0;
+    if (e < cnt) {
+      const int64_t k = skey[w][e];
+      const int64_t kp = e > 0 ? (int64_t)skey[w][e - 1] : kbefore;
+      val = (int32_t)(r0 + e);
+      if (k != kp) a = kp + 1, b = k;
+      if (r0 + e == n - 1) a2 = k + 1, b2 = nseg;
+    }
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int64_t lo = pass ? a2 : a, hi = pass ? b2 : b;
+      const int32_t v = pass ? (int32_t)n : val;
+      const bool longr = hi - lo >= 64;
+      if (!longr)
+        for (int64_t kk = lo; kk <= hi; ++kk) off[kk] = v;
+      for (uint64_t lm = __ballot(longr); lm; lm &= lm - 1) {
+        const int l = __ffsll((unsigned long long)lm) - 1;
+        const int64_t la = __shfl(lo, l), lb = __shfl(hi, l);
+        const int32_t lv = __shfl(v, l);
+        for (int64_t kk = la + lane; kk <= lb; kk += 64) off[kk] = lv;
+      }
+    }
+  }
+
   for (int i0 = 0; i0 < nsteps; i0 += kRing) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
@@ -194,7 +234,7 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
 // at a time (one coalesced load of their offsets); a ballot picks the ones
 // that cross a chunk edge, and those are dealt round-robin to the 4 waves.
 template <int D>
-__global__ __launch_bounds__(256) void seg_level2_kernel(const uint32_t* __restrict__ keys,
+__global__ __launch_bounds__(256) void seg_level2_kernel(const uint2* __restrict__ kv,
                                                          const int32_t* __restrict__ off, int64_t n, SegOut o,
                                                          const float* __restrict__ frag, double* __restrict__ gfrag) {
   constexpr int PER = (D + 63) / 64;
@@ -206,7 +246,7 @@ __global__ __launch_bounds__(256) void seg_level2_kernel(const uint32_t* __restr
   const int64_t gr0 = g * UG;
   if (gr0 >= n) return;
   const int64_t gr1 = gr0 + UG < n ? gr0 + UG : n;
-  const int64_t kf = keys[gr0], kl = keys[gr1 - 1];
+  const int64_t kf = kv[gr0].x, kl = kv[gr1 - 1].x;
   int turn = 0;  // crossing segments seen so far in this group
   for (int64_t k0 = kf; k0 <= kl; k0 += 64) {
     const int64_t kk = k0 + lane;
@@ -263,7 +303,7 @@ __global__ __launch_bounds__(256) void seg_level2_kernel(const uint32_t* __restr
 // together (interleaved by wave, combined in wave order).
 constexpr int kL3Waves = 16;
 template <int D>
-__global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint32_t* __restrict__ keys,
+__global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint2* __restrict__ kv,
                                                                    const int32_t* __restrict__ off, int64_t n,
                                                                    int64_t ngroups, SegOut o,
                                                                    const double* __restrict__ gfrag) {
@@ -279,7 +319,7 @@ __global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint32_
     if (g < ngroups) {
       const int64_t gr0 = g * UG;
       const int64_t gr1 = gr0 + UG < n ? gr0 + UG : n;
-      const int64_t kk = keys[gr0];
+      const int64_t kk = kv[gr0].x;
       s = off[kk];
       e = off[kk + 1];
       if (s < gr0 && e <= gr1) k = kk;
@@ -353,6 +393,22 @@ __global__ __launch_bounds__(256) void mean_from_sums_kernel(const double* __res
   C_new[i] = cnt[k] > 0 ? (float)(S[i] / (double)cnt[k]) : C_prev[i];
 }
 
+// Means mode: a cluster no row carries (off[k] == off[k+1]) gets count 0 and
+// keeps its previous centroid.  One thread per cluster.
+__global__ __launch_bounds__(256) void empty_fill_kernel(const int32_t* __restrict__ off, int64_t nseg, int D,
+                                                         const float* __restrict__ C_prev, float* __restrict__ C_new,
+                                                         int32_t* __restrict__ counts) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= nseg || off[k] != off[k + 1]) return;
+  counts[k] = 0;
+  if (C_new != C_prev) {  // D is a multiple of 4: copy the row as float4
+    const float4* src = reinterpret_cast<const float4*>(C_prev + k * D);
+    float4* dst = reinterpret_cast<float4*>(C_new + k * D);
+#pragma unroll 8
+    for (int d = 0; d < D / 4; ++d) dst[d] = src[d];
+  }
+}
+
 __global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_t n16, uint8_t* __restrict__ tail,
                                                    int tail_bytes) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -361,43 +417,45 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_
 }
 
 template <class T, int D>
-hipError_t seg_reduce_t(const void* X, const uint32_t* perm, const uint32_t* keys, const int32_t* off, int64_t n,
-                        uint32_t nseg, const SegOut& o, SegBuffers& buf, hipStream_t s) {
+hipError_t seg_reduce_t(const void* X, const uint2* kv, int32_t* off, int64_t n, uint32_t nseg, const SegOut& o,
+                        SegBuffers& buf, hipStream_t s) {
   const int64_t nchunks = seg_chunks(n);
   const int64_t ngroups = seg_groups(n);
   seg_level1_kernel<T, D><<<dim3((unsigned)((nchunks + 3) / 4)), dim3(256), 0, s>>>(
-      reinterpret_cast<const typename T::raw*>(X), perm, keys, n, o, buf.frag);
+      reinterpret_cast<const typename T::raw*>(X), kv, n, nseg, off, o, buf.frag);
+  if (!o.S_acc)
+    empty_fill_kernel<<<dim3((unsigned)(((int64_t)nseg + 255) / 256)), dim3(256), 0, s>>>(off, nseg, D, o.C_prev,
+                                                                                         o.C_new, o.counts);
   if (nchunks > 1) {
-    seg_level2_kernel<D><<<dim3((unsigned)ngroups), dim3(256), 0, s>>>(keys, off, n, o, buf.frag, buf.gfrag);
+    seg_level2_kernel<D><<<dim3((unsigned)ngroups), dim3(256), 0, s>>>(kv, off, n, o, buf.frag, buf.gfrag);
     if (ngroups > 1)
       seg_level3_kernel<D><<<dim3((unsigned)((ngroups + kL3Waves - 1) / kL3Waves)), dim3(kL3Waves * 64), 0, s>>>(
-          keys, off, n, ngroups, o, buf.gfrag);
+          kv, off, n, ngroups, o, buf.gfrag);
   }
   return hipGetLastError();
 }
 
 template <class T>
-hipError_t seg_reduce_d(int D, const void* X, const uint32_t* perm, const uint32_t* keys, const int32_t* off,
-                        int64_t n, uint32_t nseg, const SegOut& o, SegBuffers& buf, hipStream_t s) {
+hipError_t seg_reduce_d(int D, const void* X, const uint2* kv, int32_t* off, int64_t n, uint32_t nseg,
+                        const SegOut& o, SegBuffers& buf, hipStream_t s) {
   switch (D) {
-    case 16: return seg_reduce_t<T, 16>(X, perm, keys, off, n, nseg, o, buf, s);
-    case 32: return seg_reduce_t<T, 32>(X, perm, keys, off, n, nseg, o, buf, s);
-    case 64: return seg_reduce_t<T, 64>(X, perm, keys, off, n, nseg, o, buf, s);
-    case 128: return seg_reduce_t<T, 128>(X, perm, keys, off, n, nseg, o, buf, s);
-    case 256: return seg_reduce_t<T, 256>(X, perm, keys, off, n, nseg, o, buf, s);
+    case 16: return seg_reduce_t<T, 16>(X, kv, off, n, nseg, o, buf, s);
+    case 32: return seg_reduce_t<T, 32>(X, kv, off, n, nseg, o, buf, s);
+    case 64: return seg_reduce_t<T, 64>(X, kv, off, n, nseg, o, buf, s);
+    case 128: return seg_reduce_t<T, 128>(X, kv, off, n, nseg, o, buf, s);
+    case 256: return seg_reduce_t<T, 256>(X, kv, off, n, nseg, o, buf, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_segment_reduce(int dt, int D, const void* X, const uint32_t* perm, const uint32_t* sorted_keys,
-                                 const int32_t* off, int64_t n, uint32_t nseg, const SegOut& out, SegBuffers& buf,
-                                 hipStream_t s) {
+hipError_t launch_segment_reduce(int dt, int D, const void* X, const uint2* sorted, int32_t* off, int64_t n,
+                                 uint32_t nseg, const SegOut& out, SegBuffers& buf, hipStream_t s) {
   switch (dt) {
-    case DT_F32: return seg_reduce_d<F32>(D, X, perm, sorted_keys, off, n, nseg, out, buf, s);
-    case DT_F16: return seg_reduce_d<F16>(D, X, perm, sorted_keys, off, n, nseg, out, buf, s);
-    case DT_BF16: return seg_reduce_d<BF16>(D, X, perm, sorted_keys, off, n, nseg, out, buf, s);
+    case DT_F32: return seg_reduce_d<F32>(D, X, sorted, off, n, nseg, out, buf, s);
+    case DT_F16: return seg_reduce_d<F16>(D, X, sorted, off, n, nseg, out, buf, s);
+    case DT_BF16: return seg_reduce_d<BF16>(D, X, sorted, off, n, nseg, out, buf, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -3,12 +3,14 @@
 // to their points; article section "Flash-KMeans が変える点", second point).
 //
 // A stable least-significant-digit radix argsort of the cluster keys
-// (key = b*K + label) with 8-bit digits, then the segment offsets
-// off[k] = #{rows with key < k}.  Each digit pass is reduce-then-scan:
+// (key = b*K + label) with 8-bit digits.  Each digit pass is reduce-then-scan:
 //   hist    per-workgroup digit counts, stored digit-major [256][nblk];
 //   scan    exclusive scan of each digit row, plus the digit totals;
 //   scatter stable rank of every key inside its workgroup tile, written to
 //           digit base + workgroup offset + rank.
+// Elements travel as (key, row) pairs packed in 8 bytes, so every pass reads
+// and writes each element with one access and a digit run of a tile is one
+// contiguous piece of the output.
 // Ranks come from wave-level digit matching (eight ballots give each lane the
 // mask of lanes holding the same digit) and per-wave counters, so the output
 // order is fully determined: equal keys keep their row order.  Histogram
@@ -24,28 +26,29 @@ namespace {
 constexpr int kT = 256;
 constexpr int kIPT = kSortTile / kT;  // keys per thread per tile (16)
 
-// Key of row i.  For the first pass keys come from the labels; later passes
-// read the previous pass's output.
-struct LabelKeys {
+// Source of the (key, row) pair at position i of a pass's input.  The first
+// pass makes it from the labels (row = i); later passes read the previous
+// pass's output.
+struct LabelSrc {
   const int32_t* labels;
   int64_t N;      // rows per instance
   uint32_t K;     // centroids per instance
   int B;          // instances
   double invN;    // 1.0 / N, for the instance index
-  __device__ __forceinline__ uint32_t operator()(int64_t i) const {
+  __device__ __forceinline__ uint2 operator()(int64_t i) const {
     const int32_t l = labels[i];
     const uint32_t lab = (uint32_t)l < K ? (uint32_t)l : K - 1;  // out-of-range labels clamp (caller error)
-    if (B == 1) return lab;
+    if (B == 1) return make_uint2(lab, (uint32_t)i);
     // instance index i / N: a floating estimate corrected to the exact floor
     int64_t b = (int64_t)((double)i * invN);
     if ((b + 1) * N <= i) ++b;
     if (b * N > i) --b;
-    return (uint32_t)b * K + lab;
+    return make_uint2((uint32_t)b * K + lab, (uint32_t)i);
   }
 };
-struct BufKeys {
-  const uint32_t* keys;
-  __device__ __forceinline__ uint32_t operator()(int64_t i) const { return keys[i]; }
+struct PairSrc {
+  const uint2* kv;
+  __device__ __forceinline__ uint2 operator()(int64_t i) const { return kv[i]; }
 };
 
 // Mask of the active lanes of this wave whose 8-bit digit equals mine.
@@ -60,8 +63,8 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
   return m;
 }
 
-template <class KeyFn>
-__global__ __launch_bounds__(kT) void radix_hist_kernel(KeyFn key, int64_t n, int shift, uint32_t* __restrict__ hist,
+template <class Src>
+__global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int shift, uint32_t* __restrict__ hist,
                                                         int64_t nblk) {
   __shared__ uint32_t cnt[256];
   const int t = threadIdx.x;
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(KeyFn key, int64_t n, in
 #pragma unroll
   for (int r = 0; r < kIPT; ++r) {
     const int64_t i = base + r * kT + t;
-    d[r] = i < n ? (key(i) >> shift) & 255u : 256u;
+    d[r] = i < n ? (src(i).x >> shift) & 255u : 256u;
   }
   // LDS atomics: the counts are exact integers, so their order is irrelevant
 #pragma unroll
@@ -122,16 +125,14 @@ __global__ __launch_bounds__(kT) void radix_scan_kernel(uint32_t* __restrict__ h
 // the per-wave counts become per-wave offsets, every key lands in an LDS copy
 // of the tile sorted by digit, and the tile is written out digit run by digit
 // run, so consecutive threads write consecutive addresses.
-template <class KeyFn>
-__global__ __launch_bounds__(kT) void radix_scatter_kernel(KeyFn key, const uint32_t* __restrict__ vals_in, int64_t n,
-                                                           int shift, const uint32_t* __restrict__ hist,
+template <class Src>
+__global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, int shift,
+                                                           const uint32_t* __restrict__ hist,
                                                            const uint32_t* __restrict__ dtot, int64_t nblk,
-                                                           uint32_t* __restrict__ keys_out,
-                                                           uint32_t* __restrict__ vals_out) {
+                                                           uint2* __restrict__ out) {
   constexpr int KW = kSortTile / 4;   // keys per wave
   constexpr int RW = KW / 64;         // rounds per wave
-  __shared__ uint32_t lkey[kSortTile];
-  __shared__ uint32_t lval[kSortTile];
+  __shared__ uint2 lkv[kSortTile];
   __shared__ uint32_t gbase[256];     // global position of LDS slot 0 of digit d's run, minus lstart[d]
   __shared__ uint32_t lstart[256];    // first LDS slot of digit d
   __shared__ uint32_t wcnt[4][256];   // per-wave digit counts, then per-wave offsets
@@ -139,6 +140,17 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(KeyFn key, const uint
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int64_t blk = xcd_tile(blockIdx.x, nblk);  // the tile this workgroup sorts
+
+  // the tile's elements are loaded first, so their latency overlaps the
+  // histogram loads and scans below
+  const int64_t base = blk * kSortTile + (int64_t)w * KW;
+  uint2 e[RW];
+  uint32_t rr[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int64_t i = base + r * 64 + lane;
+    e[r] = i < n ? src(i) : make_uint2(0u, 0u);
+  }
 
   // this tile's count of digit t, from the scanned (exclusive) histogram row
   const uint32_t h0 = hist[(int64_t)t * nblk + blk];
@@ -152,20 +164,11 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(KeyFn key, const uint
   for (int ww = 0; ww < 4; ++ww) wcnt[ww][t] = 0;
   __syncthreads();
 
-  const int64_t base = blk * kSortTile + (int64_t)w * KW;
-  uint32_t kr[RW], vr[RW], rr[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int64_t i = base + r * 64 + lane;
     const bool valid = i < n;
-    kr[r] = valid ? key(i) : 0u;
-    vr[r] = valid ? (vals_in ? vals_in[i] : (uint32_t)i) : 0u;
-  }
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int64_t i = base + r * 64 + lane;
-    const bool valid = i < n;
-    const uint32_t d = (kr[r] >> shift) & 255u;
+    const uint32_t d = (e[r].x >> shift) & 255u;
     const uint64_t m = match_digit(d, valid);
     const uint32_t lrank = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
     const uint32_t before = wcnt[w][d];
@@ -187,110 +190,48 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(KeyFn key, const uint
   for (int r = 0; r < RW; ++r) {
     const int64_t i = base + r * 64 + lane;
     if (i < n) {
-      const uint32_t d = (kr[r] >> shift) & 255u;
-      const uint32_t slot = lstart[d] + wcnt[w][d] + rr[r];
-      lkey[slot] = kr[r];
-      lval[slot] = vr[r];
+      const uint32_t d = (e[r].x >> shift) & 255u;
+      lkv[lstart[d] + wcnt[w][d] + rr[r]] = e[r];
     }
   }
   __syncthreads();
   const int64_t rem = n - blk * kSortTile;
   const int cnt = rem < kSortTile ? (int)rem : kSortTile;
   for (int i = t; i < cnt; i += kT) {
-    const uint32_t k = lkey[i];
-    const uint32_t pos = gbase[(k >> shift) & 255u] + (uint32_t)i;
-    keys_out[pos] = k;
-    vals_out[pos] = lval[i];
+    const uint2 v = lkv[i];
+    out[gbase[(v.x >> shift) & 255u] + (uint32_t)i] = v;
   }
 }
 
-// off[k] for every k in [0, nseg]: row i writes the offsets of the keys in
-// (key[i-1], key[i]]; the last row also closes (key[n-1], nseg].  Keys that
-// no row carries are empty clusters: when `counts` is given they get count 0
-// and keep their previous centroid (C_new[k] = C_prev[k]).
-__global__ __launch_bounds__(kT) void segment_offsets_kernel(const uint32_t* __restrict__ keys, int64_t n,
-                                                             uint32_t nseg, int32_t* __restrict__ off,
-                                                             EmptyOut eo) {
-  // four consecutive rows per thread (one 16-byte key load; the buffer is
-  // 256-byte aligned and i0 is a multiple of 4)
-  const int64_t i0 = ((int64_t)blockIdx.x * kT + threadIdx.x) * 4;
-  if (i0 >= n) return;
-  auto clampk = [&](uint32_t v) -> int64_t { return v < nseg ? (int64_t)v : (int64_t)nseg; };
-  uint32_t kv[4];
-  if (i0 + 3 < n) {
-    const uint4 q = *reinterpret_cast<const uint4*>(keys + i0);
-    kv[0] = q.x, kv[1] = q.y, kv[2] = q.z, kv[3] = q.w;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kv[j] = i0 + j < n ? keys[i0 + j] : 0u;
-  }
-  auto empty = [&](int64_t kk) {
-    eo.counts[kk] = 0;
-    if (eo.C_new != eo.C_prev) {  // D is a multiple of 4: copy the row as float4
-      const float4* src = reinterpret_cast<const float4*>(eo.C_prev + kk * eo.D);
-      float4* dst = reinterpret_cast<float4*>(eo.C_new + kk * eo.D);
-#pragma unroll 8
-      for (int d = 0; d < eo.D / 4; ++d) dst[d] = src[d];
-    }
-  };
-  int64_t kp = i0 == 0 ? -1 : clampk(keys[i0 - 1]);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t i = i0 + j;
-    if (i >= n) break;
-    const int64_t k = clampk(kv[j]);
-    for (int64_t kk = kp + 1; kk <= k; ++kk) off[kk] = (int32_t)i;
-    if (eo.counts)
-      for (int64_t kk = kp + 1; kk < k; ++kk) empty(kk);
-    if (i == n - 1) {
-      for (int64_t kk = k + 1; kk <= (int64_t)nseg; ++kk) off[kk] = (int32_t)n;
-      if (eo.counts)
-        for (int64_t kk = k + 1; kk < (int64_t)nseg; ++kk) empty(kk);
-    }
-    kp = k;
-  }
-}
-
-template <class KeyFn>
-hipError_t one_pass(KeyFn key, const uint32_t* vals_in, int64_t n, int shift, SortBuffers& buf, uint32_t* keys_out,
-                    uint32_t* vals_out, hipStream_t s) {
+template <class Src>
+hipError_t one_pass(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out, hipStream_t s) {
   const int64_t nblk = sort_blocks(n);
-  radix_hist_kernel<KeyFn><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(key, n, shift, buf.hist, nblk);
+  radix_hist_kernel<Src><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist, nblk);
   radix_scan_kernel<<<dim3(256), dim3(kT), 0, s>>>(buf.hist, nblk, buf.dtot);
-  radix_scatter_kernel<KeyFn><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(key, vals_in, n, shift, buf.hist, buf.dtot,
-                                                                       nblk, keys_out, vals_out);
+  radix_scatter_kernel<Src><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist, buf.dtot, nblk, out);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K, SortBuffers& buf,
-                                 const uint32_t** sorted_keys, const uint32_t** perm, hipStream_t s) {
+                                 const uint2** sorted, hipStream_t s) {
   const int64_t n = N * (int64_t)B;
   const uint64_t nseg = (uint64_t)B * (uint64_t)K;
   int bits = 1;
   while (bits < 32 && (1ull << bits) < nseg) ++bits;
   const int passes = (bits + 7) / 8;
-  LabelKeys lk{labels, N, (uint32_t)K, B, 1.0 / (double)N};
-  hipError_t e = one_pass(lk, nullptr, n, 0, buf, buf.keys[0], buf.vals[0], s);
+  LabelSrc ls{labels, N, (uint32_t)K, B, 1.0 / (double)N};
+  hipError_t e = one_pass(ls, n, 0, buf, buf.kv[0], s);
   if (e != hipSuccess) return e;
   int cur = 0;
   for (int p = 1; p < passes; ++p) {
-    BufKeys bk{buf.keys[cur]};
-    e = one_pass(bk, buf.vals[cur], n, 8 * p, buf, buf.keys[cur ^ 1], buf.vals[cur ^ 1], s);
+    e = one_pass(PairSrc{buf.kv[cur]}, n, 8 * p, buf, buf.kv[cur ^ 1], s);
     if (e != hipSuccess) return e;
     cur ^= 1;
   }
-  *sorted_keys = buf.keys[cur];
-  *perm = buf.vals[cur];
+  *sorted = buf.kv[cur];
   return hipSuccess;
-}
-
-hipError_t launch_segment_offsets(const uint32_t* sorted_keys, int64_t n, uint32_t nseg, int32_t* off,
-                                  const EmptyOut& eo, hipStream_t s) {
-  const int64_t grid = (n + 4 * kT - 1) / (4 * kT);
-  segment_offsets_kernel<<<dim3((unsigned)grid), dim3(kT), 0, s>>>(sorted_keys, n, nseg, off, eo);
-  return hipGetLastError();
 }
 
 }  // namespace fkm

@@ -145,13 +145,10 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
              "assign launch");
       const int64_t nwg = (rows + cfg.rows() - 1) / cfg.rows();
       KS_HIP(launch_inertia_reduce(w.part, (int)nwg, 1, J_dev + t, nullptr, true, r.cs), "inertia launch");
-      const uint32_t* skeys = nullptr;
-      const uint32_t* perm = nullptr;
-      KS_HIP(launch_argsort_labels(lslot[sl], rows, 1, K, w.sort, &skeys, &perm, r.cs), "argsort launch");
-      KS_HIP(launch_segment_offsets(skeys, rows, (uint32_t)K, w.off, EmptyOut{nullptr, nullptr, nullptr, D}, r.cs),
-             "segment offsets launch");
+      const uint2* sorted = nullptr;
+      KS_HIP(launch_argsort_labels(lslot[sl], rows, 1, K, w.sort, &sorted, r.cs), "argsort launch");
       SegOut so{nullptr, nullptr, nullptr, S_acc, n_acc};
-      KS_HIP(launch_segment_reduce(dtype, D, xslot[sl], perm, skeys, w.off, rows, (uint32_t)K, so, w.seg, r.cs),
+      KS_HIP(launch_segment_reduce(dtype, D, xslot[sl], sorted, w.off, rows, (uint32_t)K, so, w.seg, r.cs),
              "segment reduce launch");
       KS_HIP(hipEventRecord(r.done[sl], r.cs), "event record");
       KS_HIP(hipStreamWaitEvent(r.xs, r.done[sl], 0), "stream wait");

@@ -26,7 +26,7 @@ inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Byte offsets of the scratch regions inside one workspace, 256-byte aligned.
 struct Layout {
-  size_t chat, hb, part, cnt, keys0, keys1, vals0, vals1, hist, dtot, off, frag, gfrag, total;
+  size_t chat, hb, part, cnt, kv0, kv1, hist, dtot, off, frag, gfrag, total;
 };
 
 inline Layout make_layout(int64_t N, int D, int K, int B, int dt) {
@@ -38,10 +38,8 @@ inline Layout make_layout(int64_t N, int D, int K, int B, int dt) {
   L.hb = o;    o = al256(o + (size_t)B * kpad(K) * 4);
   L.part = o;  o = al256(o + (size_t)B * assign_max_wgs(N) * 8);
   L.cnt = o;   o = al256(o + (size_t)nseg * 4);
-  L.keys0 = o; o = al256(o + (size_t)n * 4);
-  L.keys1 = o; o = al256(o + (size_t)n * 4);
-  L.vals0 = o; o = al256(o + (size_t)n * 4);
-  L.vals1 = o; o = al256(o + (size_t)n * 4);
+  L.kv0 = o;   o = al256(o + (size_t)n * 8);
+  L.kv1 = o;   o = al256(o + (size_t)n * 8);
   L.hist = o;  o = al256(o + (size_t)256 * sort_blocks(n) * 4);
   L.dtot = o;  o = al256(o + 256 * 4);
   L.off = o;   o = al256(o + (size_t)(nseg + 1) * 4);
@@ -68,10 +66,8 @@ inline Work carve(void* ws, const Layout& L) {
   w.hb = reinterpret_cast<float*>(at(L.hb));
   w.part = reinterpret_cast<double*>(at(L.part));
   w.cnt = reinterpret_cast<int32_t*>(at(L.cnt));
-  w.sort.keys[0] = reinterpret_cast<uint32_t*>(at(L.keys0));
-  w.sort.keys[1] = reinterpret_cast<uint32_t*>(at(L.keys1));
-  w.sort.vals[0] = reinterpret_cast<uint32_t*>(at(L.vals0));
-  w.sort.vals[1] = reinterpret_cast<uint32_t*>(at(L.vals1));
+  w.sort.kv[0] = reinterpret_cast<uint2*>(at(L.kv0));
+  w.sort.kv[1] = reinterpret_cast<uint2*>(at(L.kv1));
   w.sort.hist = reinterpret_cast<uint32_t*>(at(L.hist));
   w.sort.dtot = reinterpret_cast<uint32_t*>(at(L.dtot));
   w.off = reinterpret_cast<int32_t*>(at(L.off));

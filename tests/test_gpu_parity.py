@@ -121,6 +121,22 @@ def test_forced_empty_clusters(km):
     assert torch.equal(C.cpu()[0, 5], C0[0, 5]) and torch.equal(C.cpu()[0, 17], C0[0, 17])
 
 
+def test_update_all_rows_one_cluster_large_k(km):
+    """Every row in cluster 0 of K=65,536: the offsets of the other 65,535 keys
+    form one range filled after the last row, and every one of those clusters
+    is empty (count 0, previous centroid kept)."""
+    n, k, d = 100_003, 65_536, 64
+    X, _, _, _ = datagen.mixture(n, d, 4, dtype="fp16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                 weights=None, workload_code=57, seed=0)
+    lab = np.zeros((1, n), dtype=np.int32)
+    C_prev = torch.randn(1, k, d, generator=torch.Generator().manual_seed(1))
+    C_new, counts = km.update(X.cuda(), torch.from_numpy(lab).cuda(), C_prev.cuda())
+    torch.cuda.synchronize()
+    err = H.check_update(H.decode(X[0], "fp16"), lab[0], C_prev[0].numpy(), C_new.cpu()[0].numpy(),
+                         counts.cpu()[0].numpy(), k, tag="one_cluster_large_k")
+    H.log(f"update one cluster, K={k}: centroid err {err:.2e}")
+
+
 @pytest.mark.parametrize("case", ["zipf", "one_cluster", "two_clusters"])
 def test_update_long_segments(km, case):
     """Skewed labels: one segment spans many chunks and groups (the hot-cluster
