@@ -74,19 +74,69 @@ struct F32 {
   }
 };
 
-// Elements held in one 16-byte word, and the unpack of such a word to fp32.
+// Elements held in one 16-byte word: unpack to fp32, and add them into N
+// fp32 accumulators (add_if: only when `take`).  For the 16-bit types the
+// add is a two-element dot product with (1, -0) or (-0, 1): the products are
+// exact, so each accumulator receives exactly one rounded fp32 addition of
+// its element, the same value as an unpack followed by an fp32 add, in half
+// the instructions.  The -0 halves keep the multipliers from matching an
+// inline constant, whose packed 16-bit reading differs between the compiler
+// and the hardware for bf16 operands; as 32-bit literals their meaning is
+// exact.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 template <class T> struct Vec;
 template <> struct Vec<BF16> {
   static constexpr int N = 8;
   __device__ static void unpack(const uint4& v, float* o) { BF16::unpack8(v, o); }
+  __device__ __forceinline__ static void add_with(const uint4& v, float* acc, uint32_t lo, uint32_t hi) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const bf16x2 blo = __builtin_bit_cast(bf16x2, lo), bhi = __builtin_bit_cast(bf16x2, hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2 a = __builtin_bit_cast(bf16x2, w[i]);
+      acc[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(a, blo, acc[2 * i], false);
+      acc[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(a, bhi, acc[2 * i + 1], false);
+    }
+  }
+  __device__ __forceinline__ static void add(const uint4& v, float* acc) { add_with(v, acc, 0x80003F80u, 0x3F808000u); }
+  __device__ __forceinline__ static void add_if(const uint4& v, float* acc, bool take) {
+    add_with(v, acc, take ? 0x80003F80u : 0u, take ? 0x3F808000u : 0u);
+  }
 };
 template <> struct Vec<F16> {
   static constexpr int N = 8;
   __device__ static void unpack(const uint4& v, float* o) { F16::unpack8(v, o); }
+  __device__ __forceinline__ static void add_with(const uint4& v, float* acc, uint32_t lo, uint32_t hi) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const f16x2 blo = __builtin_bit_cast(f16x2, lo), bhi = __builtin_bit_cast(f16x2, hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2 a = __builtin_bit_cast(f16x2, w[i]);
+      acc[2 * i] = __builtin_amdgcn_fdot2(a, blo, acc[2 * i], false);
+      acc[2 * i + 1] = __builtin_amdgcn_fdot2(a, bhi, acc[2 * i + 1], false);
+    }
+  }
+  __device__ __forceinline__ static void add(const uint4& v, float* acc) { add_with(v, acc, 0x80003C00u, 0x3C008000u); }
+  __device__ __forceinline__ static void add_if(const uint4& v, float* acc, bool take) {
+    add_with(v, acc, take ? 0x80003C00u : 0u, take ? 0x3C008000u : 0u);
+  }
 };
 template <> struct Vec<F32> {
   static constexpr int N = 4;
   __device__ static void unpack(const uint4& v, float* o) { F32::unpack4(v, o); }
+  __device__ __forceinline__ static void add(const uint4& v, float* acc) {
+    acc[0] += __uint_as_float(v.x);
+    acc[1] += __uint_as_float(v.y);
+    acc[2] += __uint_as_float(v.z);
+    acc[3] += __uint_as_float(v.w);
+  }
+  __device__ __forceinline__ static void add_if(const uint4& v, float* acc, bool take) {
+    acc[0] += take ? __uint_as_float(v.x) : 0.f;
+    acc[1] += take ? __uint_as_float(v.y) : 0.f;
+    acc[2] += take ? __uint_as_float(v.z) : 0.f;
+    acc[3] += take ? __uint_as_float(v.w) : 0.f;
+  }
 };
 
 // One 32x32 MFMA step.  `a` / `b` are the lane's row fragments as 16-byte

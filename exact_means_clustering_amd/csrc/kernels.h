@@ -62,7 +62,7 @@ hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K,
 
 // ---- segment-local reductions ----------------------------------------------
 #ifndef FKM_SEG_ROWS
-constexpr int kSegRows = 256;    // rows of the sorted order per wave chunk (level 1)
+constexpr int kSegRows = 512;    // rows of the sorted order per wave chunk (level 1)
 #else
 constexpr int kSegRows = FKM_SEG_ROWS;
 #endif

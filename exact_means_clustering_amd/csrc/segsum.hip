@@ -61,20 +61,31 @@ __device__ __forceinline__ void finish(const SegOut& o, int64_t k, int D, int la
 // ---------------------------------------------------------------------------
 // One wave per chunk of kSegRows sorted positions.  The chunk's keys and row
 // ids are staged in LDS; the wave walks the chunk in steps of SL rows (one
-// row per lane slot, LPR lanes per row) and keeps kRing steps of row loads
+// row per lane slot q, LPR lanes per row) and keeps kRing steps of row loads
 // in flight whatever the segment boundaries.  Each lane slot accumulates its
 // rows of the current segment in fp32; when the (wave-uniform) key changes,
 // the slots are combined in a fixed butterfly and the piece is emitted:
 // finished on the spot if the whole segment lies in the chunk, otherwise
 // stored as the chunk's fragment (slot 0: the chunk's first segment, slot 1:
 // its last).
+//
+// The staging is transposed, [q][step], so a lane reads the row ids and keys
+// of four consecutive steps of its slot with one 16-byte LDS load.  Entries
+// past the chunk's end (the ring runs kRing steps ahead) hold the key
+// kNoKey and the chunk's last row id: every row load is issued
+// unconditionally (no branch around the loads keeps each ring slot in fixed
+// registers) and a step past the end adds zeros.
 #ifndef FKM_RING
 constexpr int kRing = 8;   // steps of row loads kept in flight per wave
 #else
 constexpr int kRing = FKM_RING;
 #endif
+constexpr uint32_t kNoKey = 0xFFFFFFFFu;   // no cluster key takes this value
+constexpr int kBuf = 8;                    // finished pieces buffered per wave
 
-template <class T, int D>
+// ACC selects accumulate mode (o.S_acc / o.n_acc) at compile time, so the
+// means-mode instance carries no read-modify-write code in its loop.
+template <class T, int D, bool ACC>
 __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* __restrict__ X,
                                                          const uint2* __restrict__ kv, int64_t n, uint32_t nseg,
                                                          int32_t* __restrict__ off, SegOut o,
@@ -83,34 +94,49 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
   constexpr int LPR = D * T::SZ / 16;      // lanes per row
   constexpr int SL = 64 / LPR;             // rows per step (lane slots)
   constexpr int U = kSegRows;
+  constexpr int NS = U / SL;               // steps per full chunk
+  constexpr int NSP = NS + kRing;          // staged steps per slot (with the ring's run-ahead)
   static_assert(LPR >= 1 && LPR <= 64 && U % SL == 0, "row size");
-  __shared__ uint32_t skey[4][U];
-  __shared__ uint32_t srow[4][U];
+  static_assert(kRing % 4 == 0 && NS % 4 == 0, "steps are read four at a time");
+  __shared__ __align__(16) uint32_t tkey[4][SL][NSP];
+  __shared__ __align__(16) uint32_t trow[4][SL][NSP];
+  __shared__ __align__(16) float bsum[4][kBuf][D];
+  __shared__ uint32_t bkey[4][kBuf];
+  __shared__ int32_t bkind[4][kBuf], bcnt[4][kBuf];
   const int lane = lane_id();
-  const int w = threadIdx.x >> 6;
+  // the wave index, and everything derived from it, is wave-uniform: keeping
+  // it in scalar registers makes the per-step tests scalar branches
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t c = (int64_t)blockIdx.x * 4 + w;
   const int64_t r0 = c * U;
   const bool active = r0 < n;
   const int cnt = active ? (int)(n - r0 < U ? n - r0 : U) : 0;
-  for (int e = lane; e < U; e += 64) {
-    const uint2 v = e < cnt ? kv[r0 + e] : make_uint2(0xFFFFFFFFu, 0u);
-    skey[w][e] = v.x;
-    srow[w][e] = v.y;
+  for (int e = lane; e < SL * NSP; e += 64) {
+    const int qq = e / NSP, ii = e - qq * NSP;
+    const int rr = ii * SL + qq;  // row of the chunk
+    uint32_t key = kNoKey, row = 0;
+    if (cnt > 0) {
+      const uint2 v = kv[r0 + (rr < cnt ? rr : cnt - 1)];
+      key = rr < cnt ? v.x : kNoKey;
+      row = v.y;
+    }
+    tkey[w][qq][ii] = key;
+    trow[w][qq][ii] = row;
   }
   __syncthreads();
   if (!active) return;
   const int q = lane / LPR, g = lane % LPR;
-  const uint32_t kf = skey[w][0], kl = skey[w][cnt - 1];
+  auto key_at = [&](int r) -> uint32_t { return tkey[w][r % SL][r / SL]; };  // key of chunk row r
+  const uint32_t kf = __builtin_amdgcn_readfirstlane(key_at(0));
+  const uint32_t kl = __builtin_amdgcn_readfirstlane(key_at(cnt - 1));
   const int64_t kbefore = r0 > 0 ? (int64_t)kv[r0 - 1].x : -1;  // key of the row before the chunk
   // does the chunk's first (last) segment continue from the previous (into the next) chunk?
   const bool cont_left = kbefore == (int64_t)kf;
   const bool cont_right = r0 + cnt < n && kv[r0 + cnt].x == kl;
   const int nsteps = (cnt + SL - 1) / SL;
 
-  auto load_step = [&](int i) -> uint4 {
-    const int j = i * SL + q;
-    if (i < nsteps && j < cnt) return load_nt(reinterpret_cast<const uint4*>(X + (int64_t)srow[w][j] * D) + g);
-    return make_uint4(0, 0, 0, 0);
+  auto load_row = [&](uint32_t row) -> uint4 {
+    return load_nt(reinterpret_cast<const uint4*>(X + (int64_t)row * D) + g);
   };
 
   float acc[VEC];
@@ -118,6 +144,41 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
   uint32_t cur = kf;
   int seg_start = 0;
+  // emit the piece of segment k that ends before row `end` of the chunk
+  // Finished pieces wait in a wave-private LDS buffer and are written to
+  // global memory after the loop (or when the buffer fills).  Global stores
+  // share the load counter on this architecture, so a store issued inside
+  // the loop would make the following ring waits also wait for its write
+  // acknowledgement.  Entry kinds: 0 = a segment finished in this chunk,
+  // 1 / 2 = the chunk's fragment slot 0 / 1.
+  int nb = 0;  // buffered pieces (wave-uniform)
+  auto drain = [&]() {
+    for (int b = 0; b < nb; ++b) {
+      const uint32_t k = __builtin_amdgcn_readfirstlane(bkey[w][b]);
+      const int kind = __builtin_amdgcn_readfirstlane(bkind[w][b]);
+      const int nk = __builtin_amdgcn_readfirstlane(bcnt[w][b]);
+      for (int d = lane * 4; d < D; d += 256) {
+        const float4 v = *reinterpret_cast<const float4*>(&bsum[w][b][d]);
+        if (kind == 0) {
+          if constexpr (ACC) {
+            double* sa = o.S_acc + (int64_t)k * D + d;
+            sa[0] += (double)v.x, sa[1] += (double)v.y, sa[2] += (double)v.z, sa[3] += (double)v.w;
+          } else {
+            const float fc = (float)nk;
+            *reinterpret_cast<float4*>(o.C_new + (int64_t)k * D + d) =
+                make_float4(v.x / fc, v.y / fc, v.z / fc, v.w / fc);
+          }
+        } else {
+          *reinterpret_cast<float4*>(frag + (c * 2 + (kind - 1)) * D + d) = v;
+        }
+      }
+      if (lane == 0 && kind == 0) {
+        if constexpr (ACC) o.n_acc[k] += nk;
+        else o.counts[k] = nk;
+      }
+    }
+    nb = 0;
+  };
   // emit the piece of segment k that ends before row `end` of the chunk
   auto flush = [&](uint32_t k, int end) {
     float s[VEC];
@@ -130,32 +191,30 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
     const bool left = k == kf && cont_left;
     const bool right = k == kl && cont_right;
     if (q == 0) {
-      if (!left && !right) {
-        const int64_t nk = end - seg_start;
-        if (o.S_acc) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) o.S_acc[(int64_t)k * D + g * VEC + e] += (double)s[e];
-          if (g == 0) o.n_acc[k] += nk;
-        } else {
-          const float fc = (float)nk;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) o.C_new[(int64_t)k * D + g * VEC + e] = s[e] / fc;
-          if (g == 0) o.counts[k] = (int32_t)nk;
-        }
-      } else {
-        float* fp = frag + (c * 2 + (k == kf ? 0 : 1)) * D + g * VEC;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) fp[e] = s[e];
-      }
+      for (int e = 0; e < VEC; ++e) bsum[w][nb][g * VEC + e] = s[e];
     }
+    if (lane == 0) {
+      bkey[w][nb] = k;
+      bkind[w][nb] = (left || right) ? (k == kf ? 1 : 2) : 0;
+      bcnt[w][nb] = end - seg_start;
+    }
+    if (++nb == kBuf) drain();
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
     seg_start = end;
   };
 
+  const uint4* rows4 = reinterpret_cast<const uint4*>(&trow[w][q][0]);
+  const uint4* keys4 = reinterpret_cast<const uint4*>(&tkey[w][q][0]);
+  auto pick = [](const uint4& v, int i) -> uint32_t { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
   uint4 ring[kRing];
 #pragma unroll
-  for (int u = 0; u < kRing; ++u) ring[u] = load_step(u);
+  for (int u = 0; u < kRing; u += 4) {
+    const uint4 r4 = rows4[u / 4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ring[u + t] = load_row(pick(r4, t));
+  }
 
   // Segment offsets (while the first row loads are in flight).  A row whose
   // key k differs from the previous row's key kp starts segment k:
@@ -169,8 +228,8 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
     int64_t a = 0, b = -1, a2 = 0, b2 = -1;
     int32_t val = 0;
     if (e < cnt) {
-      const int64_t k = skey[w][e];
-      const int64_t kp = e > 0 ? (int64_t)skey[w][e - 1] : kbefore;
+      const int64_t k = key_at(e);
+      const int64_t kp = e > 0 ? (int64_t)key_at(e - 1) : kbefore;
       val = (int32_t)(r0 + e);
       if (k != kp) a = kp + 1, b = k;
       if (r0 + e == n - 1) a2 = k + 1, b2 = nseg;
@@ -191,40 +250,43 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
     }
   }
 
+  // Steps are taken kRing at a time; the steps past the chunk's end in the
+  // last round add zeros to the (unchanged) last segment.
   for (int i0 = 0; i0 < nsteps; i0 += kRing) {
+    uint4 knext, rnext;
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       const int i = i0 + u;
-      if (i < nsteps) {
-        const uint4 v = ring[u];
-        ring[u] = load_step(i + kRing);
-        float f[VEC];
-        Vec<T>::unpack(v, f);
-        const int j = i * SL + q;
-        const bool valid = j < cnt;
-        const uint32_t mk = valid ? skey[w][j] : 0xFFFFFFFFu;
-        const int jl = (i * SL + SL < cnt ? i * SL + SL : cnt) - 1;
-        const uint32_t lk = skey[w][jl];  // key of the step's last row (wave-uniform)
-        if (lk == cur) {
-          // whole step inside the current segment (rows past the end hold zeros)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[e] += f[e];
-        } else {
-          // the step ends `cur` and starts one or more new segments
-          for (;;) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] += mk == cur ? f[e] : 0.f;
-            if (cur == lk) break;
-            const uint64_t above = __ballot(valid && mk > cur);
-            const int fl = __ffsll((unsigned long long)above) - 1;
-            flush(cur, i * SL + fl / LPR);
-            cur = __shfl(mk, fl);
-          }
+      if (u % 4 == 0) {
+        knext = keys4[i / 4];                 // keys of steps i .. i+3
+        rnext = rows4[(i + kRing) / 4];       // row ids of steps i+kRing .. i+kRing+3
+      }
+      const uint32_t mk = pick(knext, u % 4);
+      const bool valid = mk != kNoKey;
+      uint4 v = ring[u];
+      ring[u] = load_row(pick(rnext, u % 4));
+      const int nv = cnt - i * SL;            // valid rows in this step (uniform)
+      // key of the step's last valid row (uniform); no valid row: no boundary
+      const uint32_t lk = nv > 0 ? __builtin_amdgcn_readlane(mk, ((nv < SL ? nv : SL) - 1) * LPR) : cur;
+      if (lk == cur) {
+        // whole step inside the current segment
+        if (nv < SL && !valid) v = make_uint4(0, 0, 0, 0);
+        Vec<T>::add(v, acc);
+      } else {
+        // the step ends `cur` and starts one or more new segments
+        for (;;) {
+          Vec<T>::add_if(v, acc, mk == cur);
+          if (cur == lk) break;
+          const uint64_t above = __ballot(valid && mk > cur);
+          const int fl = __ffsll((unsigned long long)above) - 1;
+          flush(cur, i * SL + fl / LPR);
+          cur = __builtin_amdgcn_readlane(mk, fl);
         }
       }
     }
   }
   flush(cur, cnt);
+  drain();
 }
 
 // ---------------------------------------------------------------------------
@@ -421,8 +483,13 @@ hipError_t seg_reduce_t(const void* X, const uint2* kv, int32_t* off, int64_t n,
                         SegBuffers& buf, hipStream_t s) {
   const int64_t nchunks = seg_chunks(n);
   const int64_t ngroups = seg_groups(n);
-  seg_level1_kernel<T, D><<<dim3((unsigned)((nchunks + 3) / 4)), dim3(256), 0, s>>>(
-      reinterpret_cast<const typename T::raw*>(X), kv, n, nseg, off, o, buf.frag);
+  const dim3 g1((unsigned)((nchunks + 3) / 4));
+  if (o.S_acc)
+    seg_level1_kernel<T, D, true><<<g1, dim3(256), 0, s>>>(reinterpret_cast<const typename T::raw*>(X), kv, n, nseg,
+                                                          off, o, buf.frag);
+  else
+    seg_level1_kernel<T, D, false><<<g1, dim3(256), 0, s>>>(reinterpret_cast<const typename T::raw*>(X), kv, n, nseg,
+                                                           off, o, buf.frag);
   if (!o.S_acc)
     empty_fill_kernel<<<dim3((unsigned)(((int64_t)nseg + 255) / 256)), dim3(256), 0, s>>>(off, nseg, D, o.C_prev,
                                                                                          o.C_new, o.counts);
