@@ -92,8 +92,8 @@ int kmeans_update(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
   err_buf()[0] = 0;
   if (int rc = check_shape(dtype, N, D, K, B)) return rc;
   if (!X || !labels || !C_prev || !C_new) return fail(KM_EINVAL, "X, labels, C_prev and C_new must be non-null");
-  if (!aligned(X, 16) || !aligned(C_prev, 4) || !aligned(C_new, 4) || !aligned(labels, 4) || !aligned(counts, 4))
-    return fail(KM_EINVAL, "misaligned pointer (X needs 16 bytes)");
+  if (!aligned(X, 16) || !aligned(C_prev, 16) || !aligned(C_new, 16) || !aligned(labels, 4) || !aligned(counts, 4))
+    return fail(KM_EINVAL, "misaligned pointer (X and the centroid buffers need 16 bytes)");
   const Layout L = make_layout(N, D, K, B, dtype);
   if (int rc = check_ws(ws, ws_bytes, L)) return rc;
   Work w = carve(ws, L);
@@ -108,9 +108,9 @@ int kmeans_fit(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, co
   if (iters < 1) return fail(KM_EINVAL, "iters=%d must be >= 1", iters);
   if (!X || !C0 || !labels || !C_out || !inertia)
     return fail(KM_EINVAL, "X, C0, labels, C_out and inertia must be non-null");
-  if (!aligned(X, 16) || !aligned(C0, 4) || !aligned(C_out, 4) || !aligned(labels, 4) || !aligned(inertia, 8) ||
+  if (!aligned(X, 16) || !aligned(C0, 16) || !aligned(C_out, 16) || !aligned(labels, 4) || !aligned(inertia, 8) ||
       !aligned(inertia_hist, 8))
-    return fail(KM_EINVAL, "misaligned pointer (X needs 16 bytes)");
+    return fail(KM_EINVAL, "misaligned pointer (X and the centroid buffers need 16 bytes)");
   const Layout L = make_layout(N, D, K, B, dtype);
   if (int rc = check_ws(ws, ws_bytes, L)) return rc;
   Work w = carve(ws, L);

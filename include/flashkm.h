@@ -26,8 +26,9 @@
  *     rounded values; accumulation is fp32.  Ties go to the lowest index.
  *   Supported D: 16, 32, 64, 128, 256.  1 <= K <= N, B >= 1, B*N < 2^31.
  *   In-core pointers are DEVICE pointers (hipMalloc / torch CUDA tensors),
- *     contiguous; X must be 16-byte aligned, everything else naturally
- *     aligned.  The caller owns every buffer.  The in-core entry points never
+ *     contiguous; X, and the centroid buffers of kmeans_update and
+ *     kmeans_fit (C_prev, C_new, C0, C_out), must be 16-byte aligned,
+ *     everything else naturally aligned.  The caller owns every buffer.  The in-core entry points never
  *     allocate or free memory: scratch space comes from the caller's
  *     workspace `ws` of at least kmeans_workspace_bytes(...) bytes.
  *   stream is a hipStream_t passed as void* (NULL = the null stream).

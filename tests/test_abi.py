@@ -82,6 +82,10 @@ def test_validation_codes(lib):
     assert b"workspace too small" in lib.kmeans_last_error()
     assert lib.kmeans_update(FAKE, 1, 100, 128, 1, None, 20, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
     assert lib.kmeans_update(FAKE, 1, 100, 128, 1, FAKE, 20, FAKE, FAKE, None, FAKE, 0, None) == 3
+    assert lib.kmeans_update(FAKE, 1, 100, 128, 1, FAKE, 20, ctypes.c_void_p((1 << 20) + 4), FAKE, None, FAKE,
+                             1 << 30, None) == 1                              # C_prev not 16-byte aligned
+    assert lib.kmeans_fit(FAKE, 0, 100, 32, 1, FAKE, 20, 3, FAKE, ctypes.c_void_p((1 << 20) + 8), FAKE, None, FAKE,
+                          1 << 30, None) == 1                                 # C_out not 16-byte aligned
     assert lib.kmeans_fit(FAKE, 0, 100, 32, 1, FAKE, 20, 0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
     assert b"iters" in lib.kmeans_last_error()
     assert lib.kmeans_fit(FAKE, 0, 100, 32, 1, FAKE, 20, 3, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == 1
