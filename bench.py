@@ -199,11 +199,17 @@ def main():
     assign_ms = [e[0].elapsed_time(e[1]) for e in evs]
     update_ms = [e[1].elapsed_time(e[2]) for e in evs]
     # Headline: the same K steps run by the library's own Lloyd loop
-    # (kmeans_fit, one call, no host round trip between kernels).
-    km.fit(X, C0, args.warmup, ws=ws)
+    # (kmeans_fit, one call, no host round trip between kernels).  The
+    # library captures a fit into a HIP graph on the first call with a new
+    # argument list and replays it afterwards, so after the W-step warm-up
+    # one untimed call with exactly the timed arguments does the capture;
+    # the timed call replays all K iterations' kernels.
+    out = (torch.empty_like(labels), torch.empty_like(C0), torch.empty(B, dtype=torch.float64, device=dev), None)
+    km.fit(X, C0, args.warmup, ws=ws, out=out)
+    km.fit(X, C0, args.steps, ws=ws, out=out)
     torch.cuda.synchronize()
     t_start.record(stream)
-    km.fit(X, C0, args.steps, ws=ws)
+    km.fit(X, C0, args.steps, ws=ws, out=out)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -231,7 +237,7 @@ def main():
         "dtype": p.dtype,
         "data": "synthetic",
         "config": {"workload": f"{name}: " + datagen.WORKLOADS[name]["desc"], "B": B, "N": N, "D": D, "K": K,
-                   "storage": p.dtype, "accumulate": "fp32", "step": "one Lloyd iteration (assign + sort-inverse update); value from kmeans_fit over the timed steps, per-stage times from kmeans_assign / kmeans_update"},
+                   "storage": p.dtype, "accumulate": "fp32", "step": "one Lloyd iteration (assign + sort-inverse update); value from kmeans_fit over the timed steps (a replay of the fit's captured HIP graph), per-stage times from kmeans_assign / kmeans_update"},
         "assign_ms": a_ms,
         "update_ms": u_ms,
         "assign_tflops": a_tflops,

@@ -148,17 +148,34 @@ def update(X, labels, C_prev, *, C_new=None, ws=None, stream=None):
     return C_new, counts
 
 
-def fit(X, C0, iters: int, *, history: bool = False, ws=None, stream=None):
-    """Exact Lloyd iteration: returns (labels, C, inertia [B] fp64, history [iters, B] or None)."""
+def fit(X, C0, iters: int, *, history: bool = False, ws=None, stream=None, out=None):
+    """Exact Lloyd iteration: returns (labels, C, inertia [B] fp64, history [iters, B] or None).
+
+    ``out`` = (labels, C, inertia, history-or-None) reuses caller tensors for the results: calls with the same
+    buffers replay the library's captured graph of the fit instead of capturing a new one."""
     _need(X, "X")
     _need(C0, "C0", torch.float32)
     B, N, D = _shape3(X)
     K = C0.shape[-2]
     dt = _dtype(X)
-    labels = torch.empty(X.shape[:-1], dtype=torch.int32, device=X.device)
-    C = torch.empty_like(C0)
-    inertia = torch.empty(B, dtype=torch.float64, device=X.device)
-    hist = torch.empty((max(1, int(iters)), B), dtype=torch.float64, device=X.device) if history else None
+    if out is not None:
+        labels, C, inertia, hist = out
+        _need(labels, "labels", torch.int32)
+        _need(C, "C", torch.float32)
+        _need(inertia, "inertia", torch.float64)
+        if labels.numel() != B * N or C.numel() != B * K * D or inertia.numel() != B:
+            raise KMeansError(KM_EINVAL, "out tensors do not match the problem's shapes")
+        if history:
+            if hist is None or hist.numel() < max(1, int(iters)) * B:
+                raise KMeansError(KM_EINVAL, "history requested but out[3] is missing or too small")
+            _need(hist, "history", torch.float64)
+        else:
+            hist = None
+    else:
+        labels = torch.empty(X.shape[:-1], dtype=torch.int32, device=X.device)
+        C = torch.empty_like(C0)
+        inertia = torch.empty(B, dtype=torch.float64, device=X.device)
+        hist = torch.empty((max(1, int(iters)), B), dtype=torch.float64, device=X.device) if history else None
     ws = _workspace(N, D, K, B, dt, X.device, ws)
     _check(_lib.kmeans_fit(_ptr(X), dt, N, D, B, _ptr(C0), K, int(iters), _ptr(labels), _ptr(C), _ptr(inertia),
                            _ptr(hist), _ptr(ws), ws.numel(), _stream(stream)))

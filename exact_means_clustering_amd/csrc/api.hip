@@ -5,6 +5,13 @@
 
 #include "flashkm.h"
 
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <tuple>
+#include <vector>
+
 using namespace fkm;
 
 namespace {
@@ -65,6 +72,99 @@ int run_update(const void* X, int dt, int64_t N, int D, int B, const int32_t* la
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// ---- the Lloyd loop and its graph replay ------------------------------------
+struct FitArgs {
+  const void* X;
+  int dt;
+  int64_t N;
+  int D, B;
+  const float* C0;
+  int K, iters;
+  int32_t* labels;
+  float* C_out;
+  double* inertia;
+  double* hist;
+  void* ws;
+  size_t ws_bytes;
+  int dev;
+  auto tie() const { return std::tie(X, dt, N, D, B, C0, K, iters, labels, C_out, inertia, hist, ws, ws_bytes, dev); }
+  bool operator==(const FitArgs& o) const { return tie() == o.tie(); }
+};
+
+// iters x (prep, assign, inertia, argsort, segment reductions) on stream s
+int enqueue_fit(const FitArgs& a, Work& w, hipStream_t s) {
+  for (int t = 0; t < a.iters; ++t) {
+    const float* Cs = t == 0 ? a.C0 : a.C_out;
+    if (int rc = run_assign(a.X, a.dt, a.N, a.D, a.B, Cs, a.K, a.labels, nullptr, a.inertia,
+                            a.hist ? a.hist + (int64_t)t * a.B : nullptr, w, s))
+      return rc;
+    if (int rc = run_update(a.X, a.dt, a.N, a.D, a.B, a.labels, a.K, Cs, a.C_out, nullptr, w, s)) return rc;
+  }
+  return KM_OK;
+}
+
+// A fit is a fixed sequence of about a dozen kernels per iteration whose
+// arguments are only pointers and sizes, so it is captured once into a HIP
+// graph and replayed: one graph launch enqueues every kernel, which removes
+// the per-launch host overhead that dominates small problems.  Graphs are
+// kept for the last few distinct argument lists (a replay binds the same
+// buffers; their contents may change freely between calls).  Capture runs on
+// a private stream (default priority) and records kernels only.
+// FLASHKM_FIT_GRAPH=0 selects direct launches.
+constexpr size_t kGraphCache = 8;
+struct GraphEntry {
+  FitArgs key;
+  hipGraphExec_t exec;
+};
+std::mutex& graph_mutex() {
+  static std::mutex m;
+  return m;
+}
+std::vector<GraphEntry>& graph_cache() {
+  static std::vector<GraphEntry> c;
+  return c;
+}
+bool graphs_enabled() {
+  const char* e = getenv("FLASHKM_FIT_GRAPH");
+  return !(e && e[0] == '0');
+}
+
+int fit_graph(const FitArgs& a, Work& w, hipStream_t s) {
+  std::lock_guard<std::mutex> lock(graph_mutex());
+  auto& cache = graph_cache();
+  for (const GraphEntry& g : cache)
+    if (g.key == a) {
+      KM_HIP(hipGraphLaunch(g.exec, s), "graph launch");
+      return KM_OK;
+    }
+  // device queries the launches need happen now, not during the capture
+  KM_HIP(assign_prime(a.dt, a.D, assign_pick(a.dt, a.D, a.N, a.B)), "assign configuration query");
+  static hipStream_t capture[64] = {};
+  if (a.dev < 0 || a.dev >= 64) return fail(KM_EINVAL, "device index %d out of range", a.dev);
+  if (!capture[a.dev]) KM_HIP(hipStreamCreateWithFlags(&capture[a.dev], hipStreamNonBlocking), "stream create");
+  hipStream_t cs = capture[a.dev];
+  KM_HIP(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal), "graph capture begin");
+  const int rc = enqueue_fit(a, w, cs);
+  hipGraph_t graph = nullptr;
+  const hipError_t ec = hipStreamEndCapture(cs, &graph);
+  if (rc != KM_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return rc;
+  }
+  if (ec != hipSuccess) return hip_fail(ec, "graph capture end");
+  hipGraphExec_t exec = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (ei != hipSuccess) return hip_fail(ei, "graph instantiate");
+  if (cache.size() == kGraphCache) {
+    (void)hipGraphExecDestroy(cache.front().exec);
+    cache.erase(cache.begin());
+  }
+  cache.push_back(GraphEntry{a, exec});
+  KM_HIP(hipGraphLaunch(exec, s), "graph launch");
+  return KM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -115,14 +215,10 @@ int kmeans_fit(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, co
   if (int rc = check_ws(ws, ws_bytes, L)) return rc;
   Work w = carve(ws, L);
   hipStream_t s = (hipStream_t)stream;
-  for (int t = 0; t < iters; ++t) {
-    const float* Cs = t == 0 ? C0 : C_out;
-    if (int rc = run_assign(X, dtype, N, D, B, Cs, K, labels, nullptr, inertia,
-                            inertia_hist ? inertia_hist + (int64_t)t * B : nullptr, w, s))
-      return rc;
-    if (int rc = run_update(X, dtype, N, D, B, labels, K, Cs, C_out, nullptr, w, s)) return rc;
-  }
-  return KM_OK;
+  int dev = 0;
+  KM_HIP(hipGetDevice(&dev), "device query");
+  const FitArgs a{X, dtype, N, D, B, C0, K, iters, labels, C_out, inertia, inertia_hist, ws, ws_bytes, dev};
+  return graphs_enabled() ? fit_graph(a, w, s) : enqueue_fit(a, w, s);
 }
 
 const char* kmeans_last_error(void) { return err_buf(); }

@@ -416,12 +416,11 @@ hipError_t prep_t(const float* C, void* Chat, float* hb, int64_t B, int K, hipSt
   return hipGetLastError();
 }
 
+// Workgroup slots of the persistent grid on the current device: as many
+// workgroups as fit at once (queried once per thread and device).
 template <class T, int D, int PB, int W>
-hipError_t assign_t(const void* X, const void* Chat, const float* hb, int64_t N, int K, int B, int32_t* labels,
-                    float* min_d2, double* part, hipStream_t s) {
+hipError_t assign_slots(int* slots) {
   using Cfg = AssignCfg<T, D, PB, W>;
-  const int64_t jobs = (N + Cfg::ROWS - 1) / Cfg::ROWS * (int64_t)B;
-  // persistent grid: as many workgroups as fit on the device at once
   static thread_local int cached_dev = -1, cached_slots = 0;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -435,7 +434,19 @@ hipError_t assign_t(const void* X, const void* Chat, const float* hb, int64_t N,
     cached_slots = cus * (per_cu > 0 ? per_cu : 1);
     cached_dev = dev;
   }
-  const int64_t grid = jobs < cached_slots ? jobs : cached_slots;
+  *slots = cached_slots;
+  return hipSuccess;
+}
+
+template <class T, int D, int PB, int W>
+hipError_t assign_t(const void* X, const void* Chat, const float* hb, int64_t N, int K, int B, int32_t* labels,
+                    float* min_d2, double* part, hipStream_t s) {
+  using Cfg = AssignCfg<T, D, PB, W>;
+  const int64_t jobs = (N + Cfg::ROWS - 1) / Cfg::ROWS * (int64_t)B;
+  int slots = 0;
+  const hipError_t e = assign_slots<T, D, PB, W>(&slots);
+  if (e != hipSuccess) return e;
+  const int64_t grid = jobs < slots ? jobs : slots;
   assign_kernel<T, D, PB, W><<<dim3((unsigned)grid), dim3(Cfg::THREADS), 0, s>>>(
       reinterpret_cast<const typename T::raw*>(X), reinterpret_cast<const typename T::raw*>(Chat), hb, N, K, B,
       labels, min_d2, part);
@@ -472,6 +483,23 @@ hipError_t assign_cfg(AssignConfig c, const void* X, const void* Chat, const flo
   return hipErrorInvalidValue;
 }
 
+template <class T, int D>
+hipError_t assign_prime_cfg(AssignConfig c) {
+  constexpr int rb = D * T::SZ;
+  int slots = 0;
+#define FKM_CASE(PB_, W_)                                              \
+  if constexpr (cfg_compiled(rb, PB_, W_)) {                           \
+    if (c.pb == PB_ && c.waves == W_) return assign_slots<T, D, PB_, W_>(&slots); \
+  }
+  FKM_CASE(4, 4)
+  FKM_CASE(2, 8)
+  FKM_CASE(2, 4)
+  FKM_CASE(1, 8)
+  FKM_CASE(1, 4)
+#undef FKM_CASE
+  return hipErrorInvalidValue;
+}
+
 template <template <class, int> class F, class... A>
 hipError_t dispatch_dt_d(int dt, int D, A&&... a) {
   auto byd = [&](auto tag) -> hipError_t {
@@ -497,6 +525,9 @@ template <class T, int D> struct PrepF {
   static hipError_t run(const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s) {
     return prep_t<T, D>(C, Chat, hb, B, K, s);
   }
+};
+template <class T, int D> struct PrimeF {
+  static hipError_t run(AssignConfig c) { return assign_prime_cfg<T, D>(c); }
 };
 template <class T, int D> struct AssignF {
   static hipError_t run(AssignConfig c, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
@@ -546,6 +577,8 @@ hipError_t launch_assign(int dt, int D, AssignConfig cfg, const void* X, const v
                          int K, int B, int32_t* labels, float* min_d2, double* part, hipStream_t s) {
   return dispatch_dt_d<AssignF>(dt, D, cfg, X, Chat, hb, N, K, B, labels, min_d2, part, s);
 }
+
+hipError_t assign_prime(int dt, int D, AssignConfig cfg) { return dispatch_dt_d<PrimeF>(dt, D, cfg); }
 
 hipError_t launch_inertia_reduce(const double* part, int nwg, int B, double* inertia, double* hist, bool accumulate,
                                  hipStream_t s) {

@@ -39,6 +39,11 @@ hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int
 hipError_t launch_assign(int dt, int D, AssignConfig cfg, const void* X, const void* Chat, const float* hb,
                          int64_t N, int K, int B, int32_t* labels, float* min_d2, double* part, hipStream_t s);
 
+// Runs the per-device queries an assign launch with `cfg` needs (grid size),
+// without launching, so that later launches make no device query (for
+// instance while a stream is being captured into a graph).
+hipError_t assign_prime(int dt, int D, AssignConfig cfg);
+
 // inertia[b] = sum_w part[b * nwg + w] in a fixed order (added to the old
 // value when `accumulate`); also copied to hist[b] if non-null.
 hipError_t launch_inertia_reduce(const double* part, int nwg, int B, double* inertia, double* hist,

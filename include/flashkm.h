@@ -94,7 +94,8 @@ KM_API int kmeans_assign(const void* X, int32_t dtype, int64_t N, int32_t D, int
  *   C_new[b,k]  = (1/counts) * sum_{i: labels[b,i]=k} x_bi     if counts > 0
  *               = C_prev[b,k]                                 otherwise
  * Sums are fp32 within fixed chunks of the cluster-sorted order and fp64
- * across chunks; the division is IEEE fp32.  C_new may alias C_prev.
+ * across chunks; each mean is rounded once to fp32 (an fp32 division for a
+ * cluster inside one chunk, an fp64 one otherwise).  C_new may alias C_prev.
  * Labels outside [0,K) are a caller error: results are unspecified but every
  * memory access stays in bounds. */
 KM_API int kmeans_update(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
@@ -107,7 +108,12 @@ KM_API int kmeans_update(const void* X, int32_t dtype, int64_t N, int32_t D, int
  * Returns labels and inertia of the LAST assignment, and C_out = the
  * centroids after the LAST update.  inertia [B] fp64 device (required);
  * inertia_hist [iters, B] fp64 device (nullable) receives every round's
- * inertia.  C_out may alias C0.  Resuming is fit(X, C_t, iters - t). */
+ * inertia.  C_out may alias C0.  Resuming is fit(X, C_t, iters - t).
+ * The first call with a given argument list (pointers, sizes, iters, device)
+ * captures the whole fit into a HIP graph; later calls with the same list
+ * replay it with one graph launch (the last 8 lists are kept; the buffers'
+ * contents may change between calls).  Results are identical to direct
+ * launches, which the environment variable FLASHKM_FIT_GRAPH=0 selects. */
 KM_API int kmeans_fit(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
                const float* C0, int32_t K, int32_t iters,
                int32_t* labels, float* C_out, double* inertia, double* inertia_hist,
