@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="rows in the oracle timing sample")
+    ap.add_argument("--tune", action="store_true",
+                    help="time every compiled assign configuration on this shape first (kmeans_tune) and report it")
     ap.add_argument("--probe", action="store_true",
                     help="counter-collection target: one 1 GiB device copy (calibration) and one step, no timing")
     return ap.parse_args()
@@ -171,6 +173,13 @@ def main():
     C = C0.clone()
     C_next = torch.empty_like(C)
     stream = torch.cuda.current_stream()
+    tuning = None
+    if args.tune:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        pb, waves, t_ms = km.tune(X, C0, ws=ws)
+        tuning = {"pb": pb, "waves": waves, "assign_ms_per_launch": t_ms,
+                  "tuning_wall_s": time.perf_counter() - t0}
 
     def step(ev=None):
         nonlocal C, C_next
@@ -249,6 +258,8 @@ def main():
         "roofline_update": {"bound": "hbm", "achieved": u_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": u_gbs / PEAK_HBM_GBS, "algorithmic_bytes": upd_bytes},
     }
+    if tuning is not None:
+        out["tuning"] = tuning
     if not args.no_cpu_baseline:
         # rows of the oracle's timing sample: about 10-30 s of host work each
         sample = args.cpu_sample or {"c1": 65536, "c2": 1 << 20, "c3": 1 << 17, "c4": 16384}[name]

@@ -18,7 +18,8 @@ import os
 
 import torch
 
-__all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "update", "fit", "fit_streamed", "DTYPES"]
+__all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "update", "fit", "fit_streamed", "tune",
+           "tune_save", "tune_load", "DTYPES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libflashkm.so"
@@ -54,6 +55,12 @@ def _load(path=None):
     lib.kmeans_fit.restype = ctypes.c_int
     lib.kmeans_fit_streamed.argtypes = [P, i32, i64, i32, P, i32, i32, sz, P, P, P, P, P]
     lib.kmeans_fit_streamed.restype = ctypes.c_int
+    lib.kmeans_tune.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, sz, P, P, P, P]
+    lib.kmeans_tune.restype = ctypes.c_int
+    lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
+    lib.kmeans_tune_save.restype = ctypes.c_int
+    lib.kmeans_tune_load.argtypes = [ctypes.c_char_p]
+    lib.kmeans_tune_load.restype = ctypes.c_int
     lib.kmeans_last_error.argtypes = []
     lib.kmeans_last_error.restype = ctypes.c_char_p
     return lib
@@ -180,6 +187,32 @@ def fit(X, C0, iters: int, *, history: bool = False, ws=None, stream=None, out=N
     _check(_lib.kmeans_fit(_ptr(X), dt, N, D, B, _ptr(C0), K, int(iters), _ptr(labels), _ptr(C), _ptr(inertia),
                            _ptr(hist), _ptr(ws), ws.numel(), _stream(stream)))
     return labels, C, inertia, hist
+
+
+def tune(X, C, *, labels=None, ws=None, stream=None):
+    """Time every compiled assignment configuration on this shape and record the
+    fastest in the library's tuning table.  Returns (pb, waves, ms per launch)."""
+    _need(X, "X")
+    _need(C, "C", torch.float32)
+    B, N, D = _shape3(X)
+    K = C.shape[-2]
+    dt = _dtype(X)
+    labels = torch.empty(X.shape[:-1], dtype=torch.int32, device=X.device) if labels is None else labels
+    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    pb, waves, ms = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_float(0.0)
+    _check(_lib.kmeans_tune(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(labels), _ptr(ws), ws.numel(), _stream(stream),
+                            ctypes.byref(pb), ctypes.byref(waves), ctypes.byref(ms)))
+    return pb.value, waves.value, ms.value
+
+
+def tune_save(path: str):
+    """Write the tuning table as text ("dtype D N B K pb waves" per line)."""
+    _check(_lib.kmeans_tune_save(os.fsencode(path)))
+
+
+def tune_load(path: str):
+    """Add the entries of a tuning-table file (all or nothing)."""
+    _check(_lib.kmeans_tune_load(os.fsencode(path)))
 
 
 def fit_streamed(X_host, C0, iters: int, device_x_budget: int, *, history: bool = False, stream=None):

@@ -49,7 +49,7 @@ int check_ws(const void* ws, size_t ws_bytes, const Layout& L) {
 int run_assign(const void* X, int dt, int64_t N, int D, int B, const float* C, int K, int32_t* labels,
                float* min_d2, double* inertia, double* hist, Work& w, hipStream_t s) {
   KM_HIP(launch_prep(dt, D, C, w.chat, w.hb, B, K, s), "centroid prep launch");
-  const AssignConfig cfg = assign_pick(dt, D, N, B);
+  const AssignConfig cfg = assign_pick(dt, D, N, B, K);
   KM_HIP(launch_assign(dt, D, cfg, X, w.chat, w.hb, N, K, B, labels, min_d2, w.part, s), "assign launch");
   if (inertia) {
     const int64_t nwg = (N + cfg.rows() - 1) / cfg.rows();
@@ -138,7 +138,7 @@ int fit_graph(const FitArgs& a, Work& w, hipStream_t s) {
       return KM_OK;
     }
   // device queries the launches need happen now, not during the capture
-  KM_HIP(assign_prime(a.dt, a.D, assign_pick(a.dt, a.D, a.N, a.B)), "assign configuration query");
+  KM_HIP(assign_prime(a.dt, a.D, assign_pick(a.dt, a.D, a.N, a.B, a.K)), "assign configuration query");
   static hipStream_t capture[64] = {};
   if (a.dev < 0 || a.dev >= 64) return fail(KM_EINVAL, "device index %d out of range", a.dev);
   if (!capture[a.dev]) KM_HIP(hipStreamCreateWithFlags(&capture[a.dev], hipStreamNonBlocking), "stream create");
@@ -185,6 +185,51 @@ int kmeans_assign(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
   if (int rc = check_ws(ws, ws_bytes, L)) return rc;
   Work w = carve(ws, L);
   return run_assign(X, dtype, N, D, B, C, K, labels, min_d2, inertia, nullptr, w, (hipStream_t)stream);
+}
+
+int kmeans_tune(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const float* C, int32_t K,
+                int32_t* labels, void* ws, size_t ws_bytes, void* stream, int32_t* pb, int32_t* waves, float* ms) {
+  err_buf()[0] = 0;
+  if (int rc = check_shape(dtype, N, D, K, B)) return rc;
+  if (!X || !C || !labels) return fail(KM_EINVAL, "X, C and labels must be non-null");
+  if (!aligned(X, 16) || !aligned(C, 4) || !aligned(labels, 4))
+    return fail(KM_EINVAL, "misaligned pointer (X needs 16 bytes)");
+  const Layout L = make_layout(N, D, K, B, dtype);
+  if (int rc = check_ws(ws, ws_bytes, L)) return rc;
+  Work w = carve(ws, L);
+  hipStream_t s = (hipStream_t)stream;
+  struct Events {
+    hipEvent_t a = nullptr, b = nullptr;
+    ~Events() {
+      if (a) (void)hipEventDestroy(a);
+      if (b) (void)hipEventDestroy(b);
+    }
+  } ev;
+  KM_HIP(hipEventCreate(&ev.a), "event create");
+  KM_HIP(hipEventCreate(&ev.b), "event create");
+  KM_HIP(launch_prep(dtype, D, C, w.chat, w.hb, B, K, s), "centroid prep launch");
+  AssignConfig cand[8];
+  const int nc = assign_configs(dtype, D, cand, 8);
+  AssignConfig best{0, 0};
+  float best_ms = 0.f;
+  for (int i = 0; i < nc; ++i) {
+    KM_HIP(assign_prime(dtype, D, cand[i]), "assign configuration query");
+    KM_HIP(launch_assign(dtype, D, cand[i], X, w.chat, w.hb, N, K, B, labels, nullptr, w.part, s), "assign launch");
+    KM_HIP(hipEventRecord(ev.a, s), "event record");
+    for (int r = 0; r < 2; ++r)
+      KM_HIP(launch_assign(dtype, D, cand[i], X, w.chat, w.hb, N, K, B, labels, nullptr, w.part, s), "assign launch");
+    KM_HIP(hipEventRecord(ev.b, s), "event record");
+    KM_HIP(hipEventSynchronize(ev.b), "event synchronize");
+    float t = 0.f;
+    KM_HIP(hipEventElapsedTime(&t, ev.a, ev.b), "event elapsed time");
+    t *= 0.5f;
+    if (best.pb == 0 || t < best_ms) best = cand[i], best_ms = t;
+  }
+  tune_record(dtype, D, N, B, K, best);
+  if (pb) *pb = best.pb;
+  if (waves) *waves = best.waves;
+  if (ms) *ms = best_ms;
+  return KM_OK;
 }
 
 int kmeans_update(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const int32_t* labels, int32_t K,

@@ -553,10 +553,22 @@ AssignConfig env_override() {
 }
 }  // namespace
 
-AssignConfig assign_pick(int dt, int D, int64_t N, int B) {
+bool assign_config_compiled(int dt, int D, AssignConfig c) { return cfg_compiled(D * dtype_size(dt), c.pb, c.waves); }
+
+int assign_configs(int dt, int D, AssignConfig* out, int cap) {
+  const AssignConfig all[] = {{4, 4}, {2, 8}, {2, 4}, {1, 8}, {1, 4}};
+  int n = 0;
+  for (const AssignConfig& c : all)
+    if (n < cap && assign_config_compiled(dt, D, c)) out[n++] = c;
+  return n;
+}
+
+AssignConfig assign_pick(int dt, int D, int64_t N, int B, int K) {
   const int rb = D * dtype_size(dt);
   const AssignConfig o = env_override();
   if (o.pb && cfg_compiled(rb, o.pb, o.waves)) return o;
+  AssignConfig tuned;
+  if (tune_lookup(dt, D, N, B, K, &tuned) && cfg_compiled(rb, tuned.pb, tuned.waves)) return tuned;
   // Two waves per SIMD (8-wave workgroups) so one wave's argmax epilogue
   // overlaps the other's MFMAs; the deepest register blocking that still
   // leaves >= 4 workgroups per CU.

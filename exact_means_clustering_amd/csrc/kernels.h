@@ -21,10 +21,18 @@ struct AssignConfig {
   int waves;
   int rows() const { return waves * 32 * pb; }
 };
-// Configuration for a shape (dtype, D, N per instance, B instances).  The
-// environment variable FLASHKM_ASSIGN_CONFIG="pb,waves" overrides the choice
-// when that pair is compiled for the row size (tuning only).
-AssignConfig assign_pick(int dt, int D, int64_t N, int B);
+// Configuration for a shape (dtype, D, N per instance, B instances, K): the
+// environment variable FLASHKM_ASSIGN_CONFIG="pb,waves" when that pair is
+// compiled for the row size, else the tuning table's entry for the shape,
+// else a built-in rule.
+AssignConfig assign_pick(int dt, int D, int64_t N, int B, int K);
+// Is `c` compiled for rows of D elements of dtype dt?
+bool assign_config_compiled(int dt, int D, AssignConfig c);
+// The configurations compiled for the row size (at most cap); returns the count.
+int assign_configs(int dt, int D, AssignConfig* out, int cap);
+// Tuning table (thread-safe): exact-shape lookup and record.
+bool tune_lookup(int dt, int D, int64_t N, int B, int K, AssignConfig* cfg);
+void tune_record(int dt, int D, int64_t N, int B, int K, AssignConfig cfg);
 // Largest number of assign workgroups per instance over every configuration.
 inline int64_t assign_max_wgs(int64_t N) { return (N + 127) / 128; }
 

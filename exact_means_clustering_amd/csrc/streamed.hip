@@ -140,7 +140,7 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
       if (c + 1 < nch)
         if (int rc = h2d(c + 1)) return rc;
       KS_HIP(hipStreamWaitEvent(r.cs, r.copied[sl], 0), "stream wait");
-      const AssignConfig cfg = assign_pick(dtype, D, rows, 1);
+      const AssignConfig cfg = assign_pick(dtype, D, rows, 1, K);
       KS_HIP(launch_assign(dtype, D, cfg, xslot[sl], w.chat, w.hb, rows, K, 1, lslot[sl], nullptr, w.part, r.cs),
              "assign launch");
       const int64_t nwg = (rows + cfg.rows() - 1) / cfg.rows();

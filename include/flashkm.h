@@ -138,6 +138,39 @@ KM_API int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N, int
                         int32_t* labels_host, float* C_out, double* inertia_host,
                         double* inertia_hist_host, void* stream);
 
+/* Shape-keyed configuration of the assignment kernel, with a per-shape
+ * tuning cache (the pages' point about configuration tuning under dynamic
+ * shapes: paper page abstract and the article section "Flash-KMeans が変える
+ * 点", third point, which avoids re-tuning for every new shape).
+ * Assignment kernels are compiled ahead of time for a few tile
+ * configurations per row size: pb point blocks of 32 per wave and `waves`
+ * waves per workgroup.  Every configuration computes bit-identical labels
+ * (the same products in the same order); they differ only in speed.  The
+ * choice for a shape (dtype, D, N, B, K) is, in order: the environment
+ * variable FLASHKM_ASSIGN_CONFIG="pb,waves" if compiled for the row size;
+ * the tuning table's entry for exactly that shape; a built-in rule.
+ *
+ * kmeans_tune times every compiled configuration on this shape (prep once,
+ * then per configuration one warm-up and two timed assign launches on
+ * `stream`, HIP events), records the fastest in the process-wide table and
+ * returns it in *pb / *waves with its time per launch in *ms (each output
+ * nullable).  labels [B,N] receives a valid assignment.  Arguments as for
+ * kmeans_assign.  Synchronous (waits on its events).
+ *
+ * kmeans_tune_save / kmeans_tune_load write / read the table as text, one
+ * entry per line "dtype D N B K pb waves" ('#' starts a comment).  Loading
+ * adds or replaces entries; a malformed line, an unsupported shape or a
+ * configuration not compiled for the row size fails with KM_EINVAL (naming
+ * the line) and adds nothing from that file.  FLASHKM_TUNE_CACHE=<path> loads
+ * a table once, at the first configuration choice.  These two calls do not
+ * touch the GPU.  The table is shared by all threads (internally locked). */
+KM_API int kmeans_tune(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
+                       const float* C, int32_t K, int32_t* labels,
+                       void* ws, size_t ws_bytes, void* stream,
+                       int32_t* pb, int32_t* waves, float* ms);
+KM_API int kmeans_tune_save(const char* path);
+KM_API int kmeans_tune_load(const char* path);
+
 /* Text of the last error set on the calling thread ("" if none). */
 KM_API const char* kmeans_last_error(void);
 

@@ -29,7 +29,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {
         "kmeans_workspace_bytes", "kmeans_assign", "kmeans_update", "kmeans_fit", "kmeans_fit_streamed",
-        "kmeans_last_error"}
+        "kmeans_tune", "kmeans_tune_save", "kmeans_tune_load", "kmeans_last_error"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -45,6 +45,9 @@ def _sig(lib):
     lib.kmeans_update.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, P, sz, P]
     lib.kmeans_fit.argtypes = [P, i32, i64, i32, i32, P, i32, i32, P, P, P, P, P, sz, P]
     lib.kmeans_fit_streamed.argtypes = [P, i32, i64, i32, P, i32, i32, sz, P, P, P, P, P]
+    lib.kmeans_tune.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, sz, P, P, P, P]
+    lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
+    lib.kmeans_tune_load.argtypes = [ctypes.c_char_p]
     lib.kmeans_last_error.restype = ctypes.c_char_p
     return lib
 
@@ -94,6 +97,46 @@ def test_validation_codes(lib):
     assert lib.kmeans_fit_streamed(None, 1, 100, 128, FAKE, 20, 2, 1 << 30, FAKE, FAKE, FAKE, None, None) == 1
     assert lib.kmeans_fit_streamed(FAKE, 1, 100, 128, FAKE, 20, 0, 1 << 30, FAKE, FAKE, FAKE, None, None) == 1
     assert lib.kmeans_fit_streamed(FAKE, 1, 100, 120, FAKE, 20, 2, 1 << 30, FAKE, FAKE, FAKE, None, None) == 2
+    assert lib.kmeans_tune(FAKE, 2, 10, 128, 1, FAKE, 20, FAKE, FAKE, 1 << 30, None, None, None, None) == 1
+    assert lib.kmeans_tune(FAKE, 2, 100, 128, 1, FAKE, 20, FAKE, FAKE, 16, None, None, None, None) == 3
+
+
+def _table(lib, path):
+    assert lib.kmeans_tune_save(str(path).encode()) == 0, lib.kmeans_last_error()
+    return [" ".join(l.split()) for l in path.read_text().splitlines() if l.strip() and not l.startswith("#")]
+
+
+def test_tuning_table_files(lib, tmp_path):
+    """The tuning table's text format: round trip, comments, all-or-nothing
+    loading, and rejection (naming the line) of malformed lines, unsupported
+    shapes and configurations not compiled for the row size."""
+    lib = _sig(lib)
+    good = tmp_path / "good.txt"
+    good.write_text("# a comment\n2 128 8388608 1 65536 2 8\n\n1 32 1000 3 7 1 4   # trailing comment\n")
+    assert lib.kmeans_tune_load(str(good).encode()) == 0, lib.kmeans_last_error()
+    rows = _table(lib, tmp_path / "out1.txt")
+    assert "2 128 8388608 1 65536 2 8" in rows and "1 32 1000 3 7 1 4" in rows
+    # a later entry for the same shape replaces the earlier one
+    (tmp_path / "repl.txt").write_text("1 32 1000 3 7 1 8\n")
+    assert lib.kmeans_tune_load(str(tmp_path / "repl.txt").encode()) == 0
+    rows = _table(lib, tmp_path / "out2.txt")
+    assert "1 32 1000 3 7 1 8" in rows and "1 32 1000 3 7 1 4" not in rows
+    cases = [
+        ("2 64 500 1 10 2 8\n2 64 500 1\n", b":2:"),          # too few fields (line 1 must not be added)
+        ("2 64 500 1 10 2 8 9\n", b":1:"),                     # too many fields
+        ("2 96 500 1 10 1 4\n", b"unsupported shape"),          # D not supported
+        ("2 64 5 1 10 1 4\n", b"unsupported shape"),            # N < K
+        ("0 256 500 1 10 2 8\n", b"not compiled"),              # fp32 D=256 rows are 1 KB: pb=2 x 8 waves not built
+        ("2 64 500 1 10 3 8\n", b"not compiled"),
+    ]
+    for i, (text, msg) in enumerate(cases):
+        f = tmp_path / f"bad{i}.txt"
+        f.write_text(text)
+        assert lib.kmeans_tune_load(str(f).encode()) == 1, text
+        assert msg in lib.kmeans_last_error(), (text, lib.kmeans_last_error())
+    assert "2 64 500 1 10 2 8" not in _table(lib, tmp_path / "out3.txt")
+    assert lib.kmeans_tune_load(str(tmp_path / "missing.txt").encode()) == 1
+    assert lib.kmeans_tune_load(None) == 1 and lib.kmeans_tune_save(None) == 1
 
 
 def test_binding_has_no_cpu_fallback():

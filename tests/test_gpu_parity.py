@@ -280,3 +280,38 @@ def test_fit_graph_replays_match_direct_launches(km, case, monkeypatch):
     torch.cuda.synchronize()
     for a, b in zip(got, ref2):
         assert torch.equal(a, b), f"{case}: replay after an input change differs from direct launches"
+
+
+@pytest.mark.parametrize("dtype,d", [("fp16", 128), ("fp32", 32), ("bf16", 64)])
+def test_tune_and_every_config_agree(km, dtype, d, tmp_path):
+    """kmeans_tune returns a compiled configuration and records it; every
+    compiled configuration, forced through a tuning-table file, gives the same
+    labels and distances bit for bit (and the same inertia up to the order of
+    its fp64 partial sums)."""
+    X, C0, _, _ = datagen.mixture(40_009, d, 60, dtype=dtype, center_dist="normal", center_scale=2.0, sigma=1.0,
+                                  weights=None, workload_code=58, seed=d, k=211)
+    X, C = X[0].cuda(), C0[0].cuda()
+    pb, waves, ms = km.tune(X, C)
+    rb = d * X.element_size()
+    compiled = [c for c in [(4, 4), (2, 8), (2, 4), (1, 8), (1, 4)]
+                if c == (1, 4) or (c == (1, 8) and rb <= 512) or (c == (2, 4) and rb <= 512)
+                or (c == (2, 8) and rb <= 256) or (c == (4, 4) and rb <= 256)]
+    assert (pb, waves) in compiled and ms > 0
+    dt = {"fp32": 0, "fp16": 1, "bf16": 2}[dtype]
+    ref = None
+    for c in compiled:
+        f = tmp_path / f"t{c[0]}_{c[1]}.txt"
+        f.write_text(f"{dt} {d} {X.shape[0]} 1 {C.shape[0]} {c[0]} {c[1]}\n")
+        km.tune_load(str(f))
+        lab, md, J = km.assign(X, C, want_min_d2=True)
+        torch.cuda.synchronize()
+        got = (lab.cpu(), md.cpu(), float(J[0]))
+        if ref is None:
+            ref = got
+        else:
+            assert torch.equal(got[0], ref[0]), f"{dtype} D={d}: labels differ for config {c}"
+            assert torch.equal(got[1], ref[1]), f"{dtype} D={d}: distances differ for config {c}"
+            assert abs(got[2] - ref[2]) <= 1e-12 * abs(ref[2]), f"{dtype} D={d}: inertia differs for config {c}"
+    # the oracle agrees with the (shared) result
+    Xd = H.decode(X.cpu(), dtype)
+    H.check_assign(Xd, C.cpu().numpy(), ref[0].numpy(), ref[2], dtype, min_d2=ref[1].numpy(), tag=f"tune-{dtype}-{d}")
