@@ -26,6 +26,8 @@ from .fp64 import (  # noqa: F401
     decode,
     sq_dist_direct,
     assign,
+    assign_top2,
+    soft_assign,
     update,
     inertia,
     lloyd,

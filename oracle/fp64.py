@@ -11,6 +11,10 @@ Sources, cited by page title and section:
   (article), sections 論文の要点 and Flash-KMeans が変える点: the formulas of
   k-means are unchanged, the method is not an approximation, and the target is
   the classic inner loop (not seeding).
+* [GMM] "Flash-GMM: A Memory-Efficient Kernel for Scalable Soft Clustering"
+  (paper page), abstract: Gaussian-mixture soft clustering computed in one
+  pass without materialising the responsibility matrix, and border vectors
+  assigned to more than one cluster.
 
 Readings taken where the pages are silent (each is also listed in the design
 notes):
@@ -152,6 +156,57 @@ def assign(X, Chat, *, block_elems: int = 1 << 24):
         labels[r0:r0 + rows] = lab
     dmin = _rowwise_sq_dist(X, Chat[labels])
     return labels, dmin
+
+
+def assign_top2(X, Chat):
+    """Each point's two nearest centroids: the two smallest pairs (d_ik, k) in
+    lexicographic order, d_ik the direct fp64 squared distance (so an exact tie
+    puts the lower index first).  [GMM] abstract (border vectors assigned to
+    more than one cluster; the plainest hard reading is the two nearest).
+    Needs k >= 2.  Returns (labels int64 [n, 2], d fp64 [n, 2])."""
+    X = np.asarray(X, np.float64)
+    Chat = np.asarray(Chat, np.float64)
+    if Chat.shape[0] < 2:
+        raise ValueError("top-2 needs at least two centroids")
+    n = X.shape[0]
+    labels = np.empty((n, 2), dtype=np.int64)
+    dist = np.empty((n, 2))
+    rows = max(1, (1 << 22) // max(1, Chat.shape[0] * Chat.shape[1]))
+    for r0 in range(0, n, rows):
+        Dm = sq_dist_direct(X[r0:r0 + rows], Chat)
+        order = np.argsort(Dm, axis=1, kind="stable")[:, :2]   # stable: equal distances keep index order
+        labels[r0:r0 + rows] = order
+        dist[r0:r0 + rows] = np.take_along_axis(Dm, order, axis=1)
+    return labels, dist
+
+
+def soft_assign(X, Chat, log_w, sigma2: float):
+    """Gaussian-mixture E-step statistics of each point without the N x K
+    responsibility matrix.  [GMM] abstract (soft clustering; responsibilities
+    never materialised).
+
+    Readings: isotropic components sharing the variance sigma2, centred at
+    the (dtype-rounded) centroids, with log-weights log_w [k] (zeros when
+    None); the constant (2*pi*sigma2)**(-D/2) is left out.  For each point
+        a_ik = log_w_k - d_ik / (2 * sigma2),   d_ik the direct fp64 distance,
+        L_i  = log sum_k exp(a_ik)                (log of the mixture density),
+        map_i = the lowest k maximising a_ik      (its most responsible component);
+    the responsibilities are then r_ik = exp(a_ik - L_i).  The sum is taken
+    after subtracting the row maximum.  Returns (map int64 [n], L fp64 [n])."""
+    X = np.asarray(X, np.float64)
+    Chat = np.asarray(Chat, np.float64)
+    k = Chat.shape[0]
+    lw = np.zeros(k) if log_w is None else np.asarray(log_w, np.float64)
+    n = X.shape[0]
+    lab = np.empty(n, dtype=np.int64)
+    L = np.empty(n)
+    rows = max(1, (1 << 22) // max(1, k * Chat.shape[1]))
+    for r0 in range(0, n, rows):
+        A = lw[None, :] - sq_dist_direct(X[r0:r0 + rows], Chat) / (2.0 * sigma2)
+        m = A.max(axis=1)
+        lab[r0:r0 + rows] = A.argmax(axis=1)          # first maximum: lowest index
+        L[r0:r0 + rows] = m + np.log(np.exp(A - m[:, None]).sum(axis=1))
+    return lab, L
 
 
 def update(X, labels, C_prev, k: int):

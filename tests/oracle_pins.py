@@ -336,3 +336,79 @@ def pin_helpers(L):
 
 
 ALL_PINS.append(pin_helpers)
+
+
+# ------------------------------------------------ top-2 and soft assignment
+
+
+def _int_problem(rng, n, k, d):
+    """Small integer points and centroids with planted duplicate centroids
+    (exact distance ties)."""
+    X = rng.integers(-3, 4, size=(n, d))
+    C = rng.integers(-3, 4, size=(k, d))
+    C[k - 1] = C[1]                 # duplicate: exact ties at every point
+    return X, C
+
+
+def pin_top2(L):
+    """Two nearest centroids against exact integer brute force (ties to the
+    lower index), against the pinned single assignment, and K = 2."""
+    rng = np.random.default_rng(21)
+    for n, k, d in ((40, 7, 3), (25, 3, 5), (30, 9, 2)):
+        X, C = _int_problem(rng, n, k, d)
+        lab, dist = L.assign_top2(X.astype(np.float64), C.astype(np.float64))
+        for i in range(n):
+            pairs = sorted((int(((X[i] - C[j]) ** 2).sum()), j) for j in range(k))
+            assert [pairs[0][1], pairs[1][1]] == list(lab[i]), (i, pairs[:3], lab[i])
+            assert [pairs[0][0], pairs[1][0]] == list(dist[i])
+    # first column = the (separately pinned) nearest-centroid assignment
+    p = datagen.make("c2", n=3000, k=40, seed=3)
+    Xd = L.decode(p.X[0].numpy(), "fp16")
+    Ch = L.round_to_format(p.C0[0].numpy(), "fp16")
+    lab, dist = L.assign_top2(Xd, Ch)
+    lab1, d1 = L.assign(Xd, Ch)
+    assert np.array_equal(lab[:, 0], lab1) and np.array_equal(dist[:, 0], d1)
+    assert np.all(dist[:, 0] <= dist[:, 1]) and np.all(lab[:, 0] != lab[:, 1])
+    # K = 2: both centroids, nearer first
+    lab, _ = L.assign_top2(np.array([[0.0], [3.0], [1.5]]), np.array([[1.0], [2.0]]))
+    assert lab.tolist() == [[0, 1], [1, 0], [0, 1]]
+
+
+def pin_soft(L):
+    """Mixture log-density and most responsible component: closed forms, the
+    hard limit, invariants."""
+    # K = 1: L = log w0 - d / (2 s2), also far away (a sum without the
+    # maximum subtracted underflows there)
+    for s2, lw0, x in ((0.5, 0.0, [3.0, 4.0]), (3.0, -1.25, [300.0, 400.0]), (1.0, 2.0, [0.0, 0.0])):
+        lab, Lx = L.soft_assign(np.array([x]), np.zeros((1, 2)), np.array([lw0]), s2)
+        d = x[0] ** 2 + x[1] ** 2
+        assert lab[0] == 0 and abs(Lx[0] - (lw0 - d / (2 * s2))) <= 1e-12 * max(1.0, d / s2)
+    # K identical centroids: L = log K - d / (2 s2); the lowest index is most responsible
+    for K in (2, 5, 64):
+        lab, Lx = L.soft_assign(np.array([[1.0, 2.0, 2.0]]), np.tile([[0.0, 0.0, 0.0]], (K, 1)), None, 2.0)
+        assert lab[0] == 0 and abs(Lx[0] - (np.log(K) - 9.0 / 4.0)) < 1e-12
+    # two centroids symmetric about x
+    lab, Lx = L.soft_assign(np.array([[0.0, 0.0]]), np.array([[-1.0, 0.0], [1.0, 0.0]]), None, 0.25)
+    assert lab[0] == 0 and abs(Lx[0] - (np.log(2.0) - 2.0)) < 1e-12
+    # hard limit: with equal weights the most responsible component is the nearest centroid
+    p = datagen.make("c2", n=2000, k=30, seed=5)
+    Xd = L.decode(p.X[0].numpy(), "fp16")
+    Ch = L.round_to_format(p.C0[0].numpy(), "fp16")
+    near, dmin = L.assign(Xd, Ch)
+    for s2 in (0.1, 1.0, 50.0):
+        lab, Lx = L.soft_assign(Xd, Ch, None, s2)
+        assert np.array_equal(lab, near)
+        # bounds: the largest term <= L <= the largest term + log K
+        top = -dmin / (2 * s2)
+        assert np.all(Lx >= top - 1e-9 * np.abs(top)) and np.all(Lx <= top + np.log(30) + 1e-9 * np.abs(top))
+    # responsibilities sum to one; a common shift of the log-weights shifts L and keeps the mode
+    lw = np.random.default_rng(2).normal(size=30)
+    lab, Lx = L.soft_assign(Xd[:200], Ch, lw, 2.0)
+    A = lw[None, :] - L.sq_dist_direct(Xd[:200], Ch) / 4.0
+    assert np.allclose(np.exp(A - Lx[:, None]).sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.array_equal(lab, A.argmax(axis=1))
+    lab2, Lx2 = L.soft_assign(Xd[:200], Ch, lw + 3.5, 2.0)
+    assert np.array_equal(lab, lab2) and np.allclose(Lx2, Lx + 3.5, rtol=0, atol=1e-10)
+
+
+ALL_PINS += [pin_top2, pin_soft]

@@ -117,7 +117,54 @@ def _lloyd_unrounded_inertia(X, fmt, C0, iters):
     return out
 
 
+_real_top2 = L.assign_top2
+_real_soft = L.soft_assign
+
+
+def _top2_high_tie(X, Chat):
+    Dm = L.sq_dist_direct(X, Chat)
+    k = Dm.shape[1]
+    order = (k - 1 - np.argsort(Dm[:, ::-1], axis=1, kind="stable"))[:, :2]   # ties to the higher index
+    return order, np.take_along_axis(Dm, order, axis=1)
+
+
+def _top2_second_is_third(X, Chat):
+    Dm = L.sq_dist_direct(X, Chat)
+    order = np.argsort(Dm, axis=1, kind="stable")[:, [0, 2 if Dm.shape[1] > 2 else 1]]   # off by one
+    return order, np.take_along_axis(Dm, order, axis=1)
+
+
+def _soft_no_shift(X, Chat, log_w, sigma2):
+    k = np.asarray(Chat).shape[0]
+    lw = np.zeros(k) if log_w is None else np.asarray(log_w, np.float64)
+    A = lw[None, :] - L.sq_dist_direct(X, Chat) / (2.0 * sigma2)
+    with np.errstate(divide="ignore"):
+        return A.argmax(axis=1), np.log(np.exp(A).sum(axis=1))    # no maximum subtracted
+
+
+def _soft_no_half(X, Chat, log_w, sigma2):
+    return _real_soft(X, Chat, log_w, sigma2 / 2.0)                # d / sigma2 instead of d / (2 sigma2)
+
+
+def _soft_weight_sign(X, Chat, log_w, sigma2):
+    return _real_soft(X, Chat, None if log_w is None else -np.asarray(log_w), sigma2)
+
+
+def _soft_mode_last(X, Chat, log_w, sigma2):
+    k = np.asarray(Chat).shape[0]
+    lab, Lx = _real_soft(X, Chat, log_w, sigma2)
+    lw = np.zeros(k) if log_w is None else np.asarray(log_w, np.float64)
+    A = lw[None, :] - L.sq_dist_direct(X, Chat) / (2.0 * sigma2)
+    return k - 1 - A[:, ::-1].argmax(axis=1), Lx                    # ties to the highest index
+
+
 MUTANTS = {
+    "top2_high_tie": ("assign_top2", _top2_high_tie),
+    "top2_second_is_third": ("assign_top2", _top2_second_is_third),
+    "soft_no_shift": ("soft_assign", _soft_no_shift),
+    "soft_no_half": ("soft_assign", _soft_no_half),
+    "soft_weight_sign": ("soft_assign", _soft_weight_sign),
+    "soft_mode_last": ("soft_assign", _soft_mode_last),
     "assign_highest_tie": ("assign", _assign_highest_tie),
     "assign_no_cnorm": ("assign", _assign_no_cnorm),
     "assign_sign": ("assign", _assign_sign),
