@@ -18,8 +18,8 @@ import os
 
 import torch
 
-__all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "update", "fit", "fit_streamed", "tune",
-           "tune_save", "tune_load", "DTYPES"]
+__all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "assign_top2", "assign_soft", "update", "fit",
+           "fit_streamed", "tune", "tune_save", "tune_load", "DTYPES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libflashkm.so"
@@ -55,6 +55,10 @@ def _load(path=None):
     lib.kmeans_fit.restype = ctypes.c_int
     lib.kmeans_fit_streamed.argtypes = [P, i32, i64, i32, P, i32, i32, sz, P, P, P, P, P]
     lib.kmeans_fit_streamed.restype = ctypes.c_int
+    lib.kmeans_assign_top2.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, sz, P]
+    lib.kmeans_assign_top2.restype = ctypes.c_int
+    lib.kmeans_assign_soft.argtypes = [P, i32, i64, i32, i32, P, i32, P, ctypes.c_float, P, P, P, P, sz, P]
+    lib.kmeans_assign_soft.restype = ctypes.c_int
     lib.kmeans_tune.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, sz, P, P, P, P]
     lib.kmeans_tune.restype = ctypes.c_int
     lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
@@ -137,6 +141,40 @@ def assign(X, C, *, want_min_d2: bool = False, ws=None, stream=None, labels=None
     _check(_lib.kmeans_assign(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(labels), _ptr(md), _ptr(inertia),
                               _ptr(ws), ws.numel(), _stream(stream)))
     return labels, md, inertia
+
+
+def assign_top2(X, C, *, ws=None, stream=None):
+    """Two nearest centroids of every point: returns (labels [.., N, 2] int32, distances [.., N, 2] fp32)."""
+    _need(X, "X")
+    _need(C, "C", torch.float32)
+    B, N, D = _shape3(X)
+    K = C.shape[-2]
+    dt = _dtype(X)
+    labels2 = torch.empty((*X.shape[:-1], 2), dtype=torch.int32, device=X.device)
+    d2 = torch.empty((*X.shape[:-1], 2), dtype=torch.float32, device=X.device)
+    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    _check(_lib.kmeans_assign_top2(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(labels2), _ptr(d2), _ptr(ws), ws.numel(),
+                                   _stream(stream)))
+    return labels2, d2
+
+
+def assign_soft(X, C, sigma2: float, *, log_w=None, ws=None, stream=None):
+    """Gaussian-mixture soft assignment (shared variance sigma2, log-weights log_w [.., K] or None): returns
+    (most responsible component int32, log density fp32, its per-instance sum fp64 [B])."""
+    _need(X, "X")
+    _need(C, "C", torch.float32)
+    if log_w is not None:
+        _need(log_w, "log_w", torch.float32)
+    B, N, D = _shape3(X)
+    K = C.shape[-2]
+    dt = _dtype(X)
+    labels = torch.empty(X.shape[:-1], dtype=torch.int32, device=X.device)
+    logp = torch.empty(X.shape[:-1], dtype=torch.float32, device=X.device)
+    total = torch.empty(B, dtype=torch.float64, device=X.device)
+    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    _check(_lib.kmeans_assign_soft(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(log_w), float(sigma2), _ptr(labels),
+                                   _ptr(logp), _ptr(total), _ptr(ws), ws.numel(), _stream(stream)))
+    return labels, logp, total
 
 
 def update(X, labels, C_prev, *, C_new=None, ws=None, stream=None):

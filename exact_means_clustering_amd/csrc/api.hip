@@ -5,6 +5,7 @@
 
 #include "flashkm.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -185,6 +186,48 @@ int kmeans_assign(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
   if (int rc = check_ws(ws, ws_bytes, L)) return rc;
   Work w = carve(ws, L);
   return run_assign(X, dtype, N, D, B, C, K, labels, min_d2, inertia, nullptr, w, (hipStream_t)stream);
+}
+
+int kmeans_assign_top2(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const float* C, int32_t K,
+                       int32_t* labels2, float* d2, void* ws, size_t ws_bytes, void* stream) {
+  err_buf()[0] = 0;
+  if (int rc = check_shape(dtype, N, D, K, B)) return rc;
+  if (K < 2) return fail(KM_EINVAL, "top-2 assignment needs K >= 2 (K=%d)", K);
+  if (!X || !C || !labels2) return fail(KM_EINVAL, "X, C and labels2 must be non-null");
+  if (!aligned(X, 16) || !aligned(C, 4) || !aligned(labels2, 4) || !aligned(d2, 4))
+    return fail(KM_EINVAL, "misaligned pointer (X needs 16 bytes)");
+  const Layout L = make_layout(N, D, K, B, dtype);
+  if (int rc = check_ws(ws, ws_bytes, L)) return rc;
+  Work w = carve(ws, L);
+  hipStream_t s = (hipStream_t)stream;
+  KM_HIP(launch_prep(dtype, D, C, w.chat, w.hb, B, K, s), "centroid prep launch");
+  KM_HIP(launch_assign_top2(dtype, D, X, w.chat, w.hb, N, K, B, labels2, d2, s), "top-2 assign launch");
+  return KM_OK;
+}
+
+int kmeans_assign_soft(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const float* C, int32_t K,
+                       const float* log_w, float sigma2, int32_t* labels, float* log_density, double* total,
+                       void* ws, size_t ws_bytes, void* stream) {
+  err_buf()[0] = 0;
+  if (int rc = check_shape(dtype, N, D, K, B)) return rc;
+  if (!(sigma2 > 0.f) || !(sigma2 < INFINITY)) return fail(KM_EINVAL, "sigma2 must be positive and finite");
+  if (!X || !C || !labels || !log_density) return fail(KM_EINVAL, "X, C, labels and log_density must be non-null");
+  if (!aligned(X, 16) || !aligned(C, 4) || !aligned(log_w, 4) || !aligned(labels, 4) || !aligned(log_density, 4) ||
+      !aligned(total, 8))
+    return fail(KM_EINVAL, "misaligned pointer (X needs 16 bytes)");
+  const Layout L = make_layout(N, D, K, B, dtype);
+  if (int rc = check_ws(ws, ws_bytes, L)) return rc;
+  Work w = carve(ws, L);
+  hipStream_t s = (hipStream_t)stream;
+  KM_HIP(launch_prep(dtype, D, C, w.chat, w.hb, B, K, s, log_w, sigma2), "centroid prep launch");
+  const SoftArgs sa{log_w, 1.4426950408889634f / sigma2, 0.5f / sigma2};
+  KM_HIP(launch_assign_soft(dtype, D, X, w.chat, w.hb, N, K, B, labels, log_density, w.part, sa, s),
+         "soft assign launch");
+  if (total) {
+    const int64_t nwg = (N + mode_config(dtype, D).rows() - 1) / mode_config(dtype, D).rows();
+    KM_HIP(launch_inertia_reduce(w.part, (int)nwg, B, total, nullptr, false, s), "total launch");
+  }
+  return KM_OK;
 }
 
 int kmeans_tune(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const float* C, int32_t K,

@@ -41,7 +41,8 @@ namespace fkm {
 // centroid k of their instance, slots k >= K hold -inf (never chosen).
 template <class T, int D>
 __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, typename T::raw* __restrict__ Ch,
-                                                   float* __restrict__ hb, int64_t B, int K, int Kp) {
+                                                   float* __restrict__ hb, int64_t B, int K, int Kp,
+                                                   const float* __restrict__ log_w, float sigma2) {
   const int lane = lane_id();
   const int64_t slot = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (slot >= B * Kp) return;
@@ -65,7 +66,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, 
     }
   }
   ss = wave_sum_f32(ss);
-  if (lane == 0) hb[slot] = -0.5f * ss;
+  // mixture log-weights enter the score as sigma2 * log w_k (soft assignment)
+  if (lane == 0) hb[slot] = -0.5f * ss + (log_w ? sigma2 * log_w[row] : 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -117,6 +119,26 @@ __device__ __forceinline__ float max16(const f32x16& a) {
   return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, a[15]));
 }
 
+// Running top-2 update for one lane and one 32-centroid tile: the 16 scores
+// are visited in increasing centroid index, and strict comparisons keep the
+// lower index first on equal scores.
+__device__ __forceinline__ void insert_top2(const f32x16& acc, float& b1, int& i1, float& b2, int& i2, int base) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float v = acc[r];
+    const int idx = base + 8 * (r >> 2) + (r & 3);
+    if (v > b1) {
+      b2 = b1;
+      i2 = i1;
+      b1 = v;
+      i1 = idx;
+    } else if (v > b2) {
+      b2 = v;
+      i2 = idx;
+    }
+  }
+}
+
 // Running (max, argmax) update for one lane and one 32-centroid tile whose
 // maximum score is `tmax`.  `base` is the centroid index of accumulator
 // register 0 for this lane.  Centroid indices grow with the register index,
@@ -133,12 +155,23 @@ __device__ __forceinline__ void improve(const f32x16& acc, float tmax, float& be
   }
 }
 
-template <class T, int D, int PB, int W>
+// Epilogue modes (what the running per-point state is):
+//   kArgmax  (best score, its index): labels, min_d2, inertia partials;
+//   kTop2    the two best (score, index) pairs, ties to the lower index:
+//            labels [B,N,2] and both direct distances in `dist` [B,N,2];
+//   kSoft    for the Gaussian-mixture log density (the bias then carries
+//            sigma2 * log w_k): the best score and index plus the running
+//            sum l = sum_k 2^(t_k - t_best) with t_k = score_k * log2(e) / sigma2;
+//            labels = most responsible component, dist = log density, part =
+//            per-workgroup sums of it.
+enum AssignMode : int { kArgmax = 0, kTop2 = 1, kSoft = 2 };
+
+template <class T, int D, int PB, int W, int MODE>
 __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* __restrict__ X,
                                                         const typename T::raw* __restrict__ Ch,
                                                         const float* __restrict__ hb, int64_t N, int K, int B,
                                                         int32_t* __restrict__ labels, float* __restrict__ min_d2,
-                                                        double* __restrict__ part) {
+                                                        double* __restrict__ part, SoftArgs soft) {
   using Cfg = AssignCfg<T, D, PB, W>;
   constexpr int NCH = Cfg::NCH, HV = Cfg::HV, STEPS = Cfg::STEPS;
   constexpr int TK = Cfg::TK;
@@ -205,10 +238,16 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
 
     float best[PB];
     int bidx[PB];
+    float sec[PB];   // kTop2: second-best score and index
+    int sidx[PB];
+    float lsum[PB];  // kSoft: sum of 2^(t_k - t_best) over the centroids seen
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
       best[p] = -INFINITY;
       bidx[p] = 0;
+      sec[p] = -INFINITY;
+      sidx[p] = -1;
+      lsum[p] = 0.f;
     }
 
     issue_tile(0, 0);
@@ -251,13 +290,35 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
 #pragma unroll
         for (int p = 0; p < PB; ++p) {
           tmax[j][p] = max16(a[j][p]);
-          any |= tmax[j][p] > best[p];
+          any |= tmax[j][p] > (MODE == kTop2 ? sec[p] : best[p]);
         }
+      if constexpr (MODE == kSoft) {
+        // rescale the running sum to the new maximum, then add this group's
+        // terms (a group of padding rows, all -inf, changes nothing)
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int p = 0; p < PB; ++p) {
+            if (tmax[j][p] == -INFINITY) continue;
+            const float mb = tmax[j][p] > best[p] ? tmax[j][p] : best[p];
+            const float m2 = mb * soft.scale2;
+            float sum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(a[j][p][r], soft.scale2, -m2));
+            lsum[p] = lsum[p] * __builtin_amdgcn_exp2f(best[p] * soft.scale2 - m2) + sum;
+          }
+      }
       if (any) {
 #pragma unroll
         for (int j = 0; j < G; ++j)
 #pragma unroll
-          for (int p = 0; p < PB; ++p) improve(a[j][p], tmax[j][p], best[p], bidx[p], base + 32 * j);
+          for (int p = 0; p < PB; ++p) {
+            if constexpr (MODE == kTop2) {
+              if (tmax[j][p] > sec[p]) insert_top2(a[j][p], best[p], bidx[p], sec[p], sidx[p], base + 32 * j);
+            } else {
+              improve(a[j][p], tmax[j][p], best[p], bidx[p], base + 32 * j);
+            }
+          }
       }
     };
 
@@ -333,19 +394,10 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
     }
     if constexpr (Cfg::DELAY) reduce_group(prev, prev_base);
 
-    // merge the two lane halves of each point: larger score, then lower index
-    double wacc = 0.0;
-#pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const float ob = __shfl_xor(best[p], 32);
-      const int oi = __shfl_xor(bidx[p], 32);
-      if (ob > best[p] || (ob == best[p] && oi < bidx[p])) {
-        best[p] = ob;
-        bidx[p] = oi;
-      }
-      // squared distance to the chosen centroid, computed directly (no
-      // cancellation): each half sums its dims, the halves then add.
-      const uint4* cr = reinterpret_cast<const uint4*>(Cb + (int64_t)bidx[p] * D) + h * HV;
+    // squared distance of point block p to centroid k, computed directly (no
+    // cancellation): each lane half sums its dims, the halves then add.
+    auto direct_d2 = [&](int p, int k) -> float {
+      const uint4* cr = reinterpret_cast<const uint4*>(Cb + (int64_t)k * D) + h * HV;
       float part_d = 0.f;
 #pragma unroll
       for (int v = 0; v < HV; ++v) {
@@ -359,22 +411,80 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
         }
       }
       const float other = __shfl_xor(part_d, 32);
-      const float d2 = h == 0 ? part_d + other : other + part_d;
+      return h == 0 ? part_d + other : other + part_d;
+    };
+    // larger score, then lower index
+    auto better = [](float s1, int i1, float s2, int i2) { return s1 > s2 || (s1 == s2 && i1 < i2); };
+
+    // merge the two lane halves of each point and write its results
+    double wacc = 0.0;
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      const float ob = __shfl_xor(best[p], 32);
+      const int oi = __shfl_xor(bidx[p], 32);
       const int64_t n = p0 + p * 32 + col;
-      if (h == 0 && n < N) {
-        labels[(int64_t)b * N + n] = bidx[p];
-        if (min_d2) min_d2[(int64_t)b * N + n] = d2;
-        wacc += (double)d2;
+      const bool writer = h == 0 && n < N;
+      if constexpr (MODE == kTop2) {
+        const float os = __shfl_xor(sec[p], 32);
+        const int oj = __shfl_xor(sidx[p], 32);
+        int k1, k2;
+        if (better(best[p], bidx[p], ob, oi)) {
+          k1 = bidx[p];
+          k2 = better(sec[p], sidx[p], ob, oi) ? sidx[p] : oi;
+        } else {
+          k1 = oi;
+          k2 = better(best[p], bidx[p], os, oj) ? bidx[p] : oj;
+        }
+        const float d1 = direct_d2(p, k1), d2 = direct_d2(p, k2);
+        if (writer) {
+          const int64_t o = 2 * ((int64_t)b * N + n);
+          labels[o] = k1;
+          labels[o + 1] = k2;
+          if (min_d2) {
+            min_d2[o] = d1;
+            min_d2[o + 1] = d2;
+          }
+        }
+      } else {
+        float l = 0.f;
+        if constexpr (MODE == kSoft) {
+          // combine the halves' sums at the larger maximum
+          const float ol = __shfl_xor(lsum[p], 32);
+          const float m2 = (ob > best[p] ? ob : best[p]) * soft.scale2;
+          l = lsum[p] * __builtin_amdgcn_exp2f(best[p] * soft.scale2 - m2) +
+              ol * __builtin_amdgcn_exp2f(ob * soft.scale2 - m2);
+        }
+        if (better(ob, oi, best[p], bidx[p])) {
+          best[p] = ob;
+          bidx[p] = oi;
+        }
+        const float d2 = direct_d2(p, bidx[p]);
+        if (writer) {
+          labels[(int64_t)b * N + n] = bidx[p];
+          if constexpr (MODE == kSoft) {
+            // log sum_k w_k exp(-d_k / (2 sigma2)) = a_best + ln(sum_k 2^(t_k - t_best)),
+            // anchored on the direct distance of the most responsible centroid
+            const float lw = soft.log_w ? soft.log_w[(int64_t)b * K + bidx[p]] : 0.f;
+            const float L = lw - d2 * soft.inv2s2 + __builtin_amdgcn_logf(l) * 0.693147180559945309f;
+            min_d2[(int64_t)b * N + n] = L;
+            wacc += (double)L;
+          } else {
+            if (min_d2) min_d2[(int64_t)b * N + n] = d2;
+            wacc += (double)d2;
+          }
+        }
       }
     }
-    wacc = wave_sum_f64(wacc);
-    if (lane == 0) wsum[w] = wacc;
-    __syncthreads();
-    if (tid == 0) {
-      double tot = 0.0;
+    if constexpr (MODE != kTop2) {
+      wacc = wave_sum_f64(wacc);
+      if (lane == 0) wsum[w] = wacc;
+      __syncthreads();
+      if (tid == 0) {
+        double tot = 0.0;
 #pragma unroll
-      for (int i = 0; i < W; ++i) tot += wsum[i];
-      part[(int64_t)b * nblk + blk] = tot;
+        for (int i = 0; i < W; ++i) tot += wsum[i];
+        part[(int64_t)b * nblk + blk] = tot;
+      }
     }
   }
 }
@@ -408,17 +518,18 @@ __global__ __launch_bounds__(1024) void inertia_reduce_kernel(const double* __re
 namespace {
 
 template <class T, int D>
-hipError_t prep_t(const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s) {
+hipError_t prep_t(const float* C, void* Chat, float* hb, int64_t B, int K, const float* log_w, float sigma2,
+                  hipStream_t s) {
   const int64_t slots = B * kpad(K);
   const int64_t grid = (slots + 3) / 4;
   prep_kernel<T, D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(C, reinterpret_cast<typename T::raw*>(Chat), hb, B,
-                                                                K, (int)kpad(K));
+                                                                K, (int)kpad(K), log_w, sigma2);
   return hipGetLastError();
 }
 
 // Workgroup slots of the persistent grid on the current device: as many
 // workgroups as fit at once (queried once per thread and device).
-template <class T, int D, int PB, int W>
+template <class T, int D, int PB, int W, int MODE>
 hipError_t assign_slots(int* slots) {
   using Cfg = AssignCfg<T, D, PB, W>;
   static thread_local int cached_dev = -1, cached_slots = 0;
@@ -428,8 +539,8 @@ hipError_t assign_slots(int* slots) {
   if (dev != cached_dev) {
     int cus = 0, per_cu = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, assign_kernel<T, D, PB, W>, Cfg::THREADS, 0)) !=
-        hipSuccess)
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, assign_kernel<T, D, PB, W, MODE>, Cfg::THREADS,
+                                                          0)) != hipSuccess)
       return e;
     cached_slots = cus * (per_cu > 0 ? per_cu : 1);
     cached_dev = dev;
@@ -438,18 +549,18 @@ hipError_t assign_slots(int* slots) {
   return hipSuccess;
 }
 
-template <class T, int D, int PB, int W>
+template <class T, int D, int PB, int W, int MODE>
 hipError_t assign_t(const void* X, const void* Chat, const float* hb, int64_t N, int K, int B, int32_t* labels,
-                    float* min_d2, double* part, hipStream_t s) {
+                    float* min_d2, double* part, SoftArgs soft, hipStream_t s) {
   using Cfg = AssignCfg<T, D, PB, W>;
   const int64_t jobs = (N + Cfg::ROWS - 1) / Cfg::ROWS * (int64_t)B;
   int slots = 0;
-  const hipError_t e = assign_slots<T, D, PB, W>(&slots);
+  const hipError_t e = assign_slots<T, D, PB, W, MODE>(&slots);
   if (e != hipSuccess) return e;
   const int64_t grid = jobs < slots ? jobs : slots;
-  assign_kernel<T, D, PB, W><<<dim3((unsigned)grid), dim3(Cfg::THREADS), 0, s>>>(
+  assign_kernel<T, D, PB, W, MODE><<<dim3((unsigned)grid), dim3(Cfg::THREADS), 0, s>>>(
       reinterpret_cast<const typename T::raw*>(X), reinterpret_cast<const typename T::raw*>(Chat), hb, N, K, B,
-      labels, min_d2, part);
+      labels, min_d2, part, soft);
   return hipGetLastError();
 }
 
@@ -465,21 +576,31 @@ constexpr bool cfg_compiled(int row_bytes, int pb, int waves) {
   return false;
 }
 
-template <class T, int D>
+// The top-2 and soft epilogues are compiled for one configuration per row
+// size (one point block per wave; 8 waves when the row allows it).
+constexpr int mode_waves(int row_bytes) { return row_bytes <= 512 ? 8 : 4; }
+
+template <class T, int D, int MODE>
 hipError_t assign_cfg(AssignConfig c, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
-                      int32_t* labels, float* min_d2, double* part, hipStream_t s) {
+                      int32_t* labels, float* min_d2, double* part, SoftArgs soft, hipStream_t s) {
   constexpr int rb = D * T::SZ;
-#define FKM_CASE(PB_, W_)                                                                \
-  if constexpr (cfg_compiled(rb, PB_, W_)) {                                             \
-    if (c.pb == PB_ && c.waves == W_)                                                    \
-      return assign_t<T, D, PB_, W_>(X, Chat, hb, N, K, B, labels, min_d2, part, s);     \
-  }
-  FKM_CASE(4, 4)
-  FKM_CASE(2, 8)
-  FKM_CASE(2, 4)
-  FKM_CASE(1, 8)
-  FKM_CASE(1, 4)
+  if constexpr (MODE == kArgmax) {
+#define FKM_CASE(PB_, W_)                                                                      \
+    if constexpr (cfg_compiled(rb, PB_, W_)) {                                                 \
+      if (c.pb == PB_ && c.waves == W_)                                                        \
+        return assign_t<T, D, PB_, W_, MODE>(X, Chat, hb, N, K, B, labels, min_d2, part, soft, s); \
+    }
+    FKM_CASE(4, 4)
+    FKM_CASE(2, 8)
+    FKM_CASE(2, 4)
+    FKM_CASE(1, 8)
+    FKM_CASE(1, 4)
 #undef FKM_CASE
+  } else {
+    constexpr int MW = mode_waves(rb);
+    if (c.pb == 1 && c.waves == MW)
+      return assign_t<T, D, 1, MW, MODE>(X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -489,7 +610,7 @@ hipError_t assign_prime_cfg(AssignConfig c) {
   int slots = 0;
 #define FKM_CASE(PB_, W_)                                              \
   if constexpr (cfg_compiled(rb, PB_, W_)) {                           \
-    if (c.pb == PB_ && c.waves == W_) return assign_slots<T, D, PB_, W_>(&slots); \
+    if (c.pb == PB_ && c.waves == W_) return assign_slots<T, D, PB_, W_, kArgmax>(&slots); \
   }
   FKM_CASE(4, 4)
   FKM_CASE(2, 8)
@@ -522,17 +643,23 @@ hipError_t dispatch_dt_d(int dt, int D, A&&... a) {
 }
 
 template <class T, int D> struct PrepF {
-  static hipError_t run(const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s) {
-    return prep_t<T, D>(C, Chat, hb, B, K, s);
+  static hipError_t run(const float* C, void* Chat, float* hb, int64_t B, int K, const float* log_w, float sigma2,
+                        hipStream_t s) {
+    return prep_t<T, D>(C, Chat, hb, B, K, log_w, sigma2, s);
   }
 };
 template <class T, int D> struct PrimeF {
   static hipError_t run(AssignConfig c) { return assign_prime_cfg<T, D>(c); }
 };
 template <class T, int D> struct AssignF {
-  static hipError_t run(AssignConfig c, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
-                        int32_t* labels, float* min_d2, double* part, hipStream_t s) {
-    return assign_cfg<T, D>(c, X, Chat, hb, N, K, B, labels, min_d2, part, s);
+  static hipError_t run(int mode, AssignConfig c, const void* X, const void* Chat, const float* hb, int64_t N, int K,
+                        int B, int32_t* labels, float* min_d2, double* part, SoftArgs soft, hipStream_t s) {
+    switch (mode) {
+      case kArgmax: return assign_cfg<T, D, kArgmax>(c, X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
+      case kTop2: return assign_cfg<T, D, kTop2>(c, X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
+      case kSoft: return assign_cfg<T, D, kSoft>(c, X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
+      default: return hipErrorInvalidValue;
+    }
   }
 };
 
@@ -581,13 +708,29 @@ AssignConfig assign_pick(int dt, int D, int64_t N, int B, int K) {
   return AssignConfig{1, 4};
 }
 
-hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s) {
-  return dispatch_dt_d<PrepF>(dt, D, C, Chat, hb, B, K, s);
+hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s,
+                       const float* log_w, float sigma2) {
+  return dispatch_dt_d<PrepF>(dt, D, C, Chat, hb, B, K, log_w, sigma2, s);
 }
 
 hipError_t launch_assign(int dt, int D, AssignConfig cfg, const void* X, const void* Chat, const float* hb, int64_t N,
                          int K, int B, int32_t* labels, float* min_d2, double* part, hipStream_t s) {
-  return dispatch_dt_d<AssignF>(dt, D, cfg, X, Chat, hb, N, K, B, labels, min_d2, part, s);
+  return dispatch_dt_d<AssignF>(dt, D, (int)kArgmax, cfg, X, Chat, hb, N, K, B, labels, min_d2, part, SoftArgs{},
+                                s);
+}
+
+AssignConfig mode_config(int dt, int D) { return AssignConfig{1, mode_waves(D * dtype_size(dt))}; }
+
+hipError_t launch_assign_top2(int dt, int D, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
+                              int32_t* labels2, float* d2, hipStream_t s) {
+  return dispatch_dt_d<AssignF>(dt, D, (int)kTop2, mode_config(dt, D), X, Chat, hb, N, K, B, labels2, d2,
+                                (double*)nullptr, SoftArgs{}, s);
+}
+
+hipError_t launch_assign_soft(int dt, int D, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
+                              int32_t* labels, float* logp, double* part, SoftArgs soft, hipStream_t s) {
+  return dispatch_dt_d<AssignF>(dt, D, (int)kSoft, mode_config(dt, D), X, Chat, hb, N, K, B, labels, logp, part,
+                                soft, s);
 }
 
 hipError_t assign_prime(int dt, int D, AssignConfig cfg) { return dispatch_dt_d<PrimeF>(dt, D, cfg); }

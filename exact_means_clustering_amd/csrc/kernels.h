@@ -40,12 +40,31 @@ inline int64_t assign_max_wgs(int64_t N) { return (N + 127) / 128; }
 __host__ __device__ inline int64_t kpad(int K) { return ((int64_t)K + 255) / 256 * 256; }
 // Chat[b,k] = RNE(C[b,k] -> dtype) and hb[b * kpad(K) + k] = -0.5 * ||Chat[b,k]||^2
 // for k < K; hb[b * kpad(K) + k] = -inf for K <= k < kpad(K).
-hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s);
+// With log_w (soft assignment) the bias also carries sigma2 * log_w[b * K + k].
+hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s,
+                       const float* log_w = nullptr, float sigma2 = 0.f);
 
 // Fused distance + running argmin.  part[b * nwg + wg] receives each
 // workgroup's fp64 sum of min_d2 (nwg = ceil(N / rows_per_wg(pb))).
 hipError_t launch_assign(int dt, int D, AssignConfig cfg, const void* X, const void* Chat, const float* hb,
                          int64_t N, int K, int B, int32_t* labels, float* min_d2, double* part, hipStream_t s);
+
+// Two nearest centroids of every point: labels2 [B,N,2] (nearer first, ties
+// to the lower index), d2 [B,N,2] their direct squared distances (nullable).
+hipError_t launch_assign_top2(int dt, int D, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
+                              int32_t* labels2, float* d2, hipStream_t s);
+// Gaussian-mixture soft assignment (the bias must come from launch_prep with
+// the log-weights and sigma2): labels = most responsible component, logp =
+// log sum_k w_k exp(-||x - c_k||^2 / (2 sigma2)), part = per-workgroup sums.
+struct SoftArgs {
+  const float* log_w;  // [B,K] or null (all zero)
+  float scale2;        // log2(e) / sigma2
+  float inv2s2;        // 1 / (2 sigma2)
+};
+hipError_t launch_assign_soft(int dt, int D, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
+                              int32_t* labels, float* logp, double* part, SoftArgs soft, hipStream_t s);
+// Configuration of the top-2 and soft launches (rows per workgroup: rows()).
+AssignConfig mode_config(int dt, int D);
 
 // Runs the per-device queries an assign launch with `cfg` needs (grid size),
 // without launching, so that later launches make no device query (for

@@ -28,9 +28,10 @@
  *   In-core pointers are DEVICE pointers (hipMalloc / torch CUDA tensors),
  *     contiguous; X, and the centroid buffers of kmeans_update and
  *     kmeans_fit (C_prev, C_new, C0, C_out), must be 16-byte aligned,
- *     everything else naturally aligned.  The caller owns every buffer.  The in-core entry points never
- *     allocate or free memory: scratch space comes from the caller's
- *     workspace `ws` of at least kmeans_workspace_bytes(...) bytes.
+ *     everything else naturally aligned.  The caller owns every buffer.
+ *     The in-core entry points never allocate or free memory: scratch space
+ *     comes from the caller's workspace `ws` of at least
+ *     kmeans_workspace_bytes(...) bytes.
  *   stream is a hipStream_t passed as void* (NULL = the null stream).
  *     In-core calls only enqueue work on it; results are valid once the
  *     stream has been synchronised.  Calls that share a workspace must be
@@ -137,6 +138,36 @@ KM_API int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N, int
                         const float* C0, int32_t K, int32_t iters, size_t device_x_budget,
                         int32_t* labels_host, float* C_out, double* inertia_host,
                         double* inertia_hist_host, void* stream);
+
+/* Multi-assignment epilogue (the "Flash-GMM: A Memory-Efficient Kernel for
+ * Scalable Soft Clustering" page, abstract: border vectors assigned to more
+ * than one cluster).  The assignment kernel with a top-2 running state:
+ *   labels2[b,i,0..1] = the two smallest (d_ik, k) pairs, d_ik the squared
+ *                       distance to the dtype-rounded centroid (exact ties:
+ *                       lower index first),
+ *   d2[b,i,0..1]      = those two distances, computed directly (nullable).
+ * Needs K >= 2.  Arguments otherwise as kmeans_assign; asynchronous. */
+KM_API int kmeans_assign_top2(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
+                              const float* C, int32_t K, int32_t* labels2, float* d2,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Soft-assignment epilogue (same page, abstract: Gaussian-mixture soft
+ * clustering in one pass without materialising the N x K responsibility
+ * matrix).  Components are isotropic with the shared variance sigma2 > 0,
+ * centred at the dtype-rounded centroids, with log-weights log_w [B,K] fp32
+ * (NULL = all zero); the constant (2 pi sigma2)^(-D/2) is left out.  With
+ * a_ik = log_w_k - ||x_i - c_k||^2 / (2 sigma2):
+ *   log_density[b,i] = log sum_k exp(a_ik)          (fp32; responsibilities
+ *                      are r_ik = exp(a_ik - log_density[b,i])),
+ *   labels[b,i]      = the most responsible component (lowest k on ties),
+ *   total[b]         = sum_i log_density[b,i] in fp64 (nullable).
+ * The kernel keeps a running maximum and a running sum of exponentials per
+ * point (base 2, fp32) and anchors the result on the directly computed
+ * distance of the most responsible centroid.  Asynchronous. */
+KM_API int kmeans_assign_soft(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
+                              const float* C, int32_t K, const float* log_w, float sigma2,
+                              int32_t* labels, float* log_density, double* total,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* Shape-keyed configuration of the assignment kernel, with a per-shape
  * tuning cache (the pages' point about configuration tuning under dynamic

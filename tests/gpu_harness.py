@@ -28,6 +28,12 @@ TOL_CENTROID = 1e-4
 TOL_TIE = 1e-5
 
 
+def rowwise_sq_dist(A, B) -> np.ndarray:
+    """Row i: sum_d (A[i, d] - B[i, d])**2 in fp64."""
+    diff = np.asarray(A, np.float64) - np.asarray(B, np.float64)
+    return np.einsum("ij,ij->i", diff, diff)
+
+
 def log(msg):
     print(f"[parity] {msg}", flush=True)
     sys.stdout.flush()

@@ -29,7 +29,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {
         "kmeans_workspace_bytes", "kmeans_assign", "kmeans_update", "kmeans_fit", "kmeans_fit_streamed",
-        "kmeans_tune", "kmeans_tune_save", "kmeans_tune_load", "kmeans_last_error"}
+        "kmeans_assign_top2", "kmeans_assign_soft", "kmeans_tune", "kmeans_tune_save", "kmeans_tune_load",
+        "kmeans_last_error"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -46,6 +47,8 @@ def _sig(lib):
     lib.kmeans_fit.argtypes = [P, i32, i64, i32, i32, P, i32, i32, P, P, P, P, P, sz, P]
     lib.kmeans_fit_streamed.argtypes = [P, i32, i64, i32, P, i32, i32, sz, P, P, P, P, P]
     lib.kmeans_tune.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, sz, P, P, P, P]
+    lib.kmeans_assign_top2.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, sz, P]
+    lib.kmeans_assign_soft.argtypes = [P, i32, i64, i32, i32, P, i32, P, ctypes.c_float, P, P, P, P, sz, P]
     lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
     lib.kmeans_tune_load.argtypes = [ctypes.c_char_p]
     lib.kmeans_last_error.restype = ctypes.c_char_p
@@ -99,6 +102,18 @@ def test_validation_codes(lib):
     assert lib.kmeans_fit_streamed(FAKE, 1, 100, 120, FAKE, 20, 2, 1 << 30, FAKE, FAKE, FAKE, None, None) == 2
     assert lib.kmeans_tune(FAKE, 2, 10, 128, 1, FAKE, 20, FAKE, FAKE, 1 << 30, None, None, None, None) == 1
     assert lib.kmeans_tune(FAKE, 2, 100, 128, 1, FAKE, 20, FAKE, FAKE, 16, None, None, None, None) == 3
+    assert lib.kmeans_assign_top2(FAKE, 2, 100, 128, 1, FAKE, 1, FAKE, None, FAKE, 1 << 30, None) == 1   # K < 2
+    assert b"K >= 2" in lib.kmeans_last_error()
+    assert lib.kmeans_assign_top2(FAKE, 2, 100, 128, 1, FAKE, 5, None, None, FAKE, 1 << 30, None) == 1
+    assert lib.kmeans_assign_top2(FAKE, 2, 100, 128, 1, FAKE, 5, FAKE, None, FAKE, 16, None) == 3
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.kmeans_assign_soft(FAKE, 2, 100, 128, 1, FAKE, 5, None, bad, FAKE, FAKE, None, FAKE, 1 << 30,
+                                      None) == 1
+        assert b"sigma2" in lib.kmeans_last_error()
+    assert lib.kmeans_assign_soft(FAKE, 2, 100, 128, 1, FAKE, 5, None, 1.0, FAKE, None, None, FAKE, 1 << 30,
+                                  None) == 1
+    assert lib.kmeans_assign_soft(FAKE, 2, 100, 128, 1, FAKE, 5, ctypes.c_void_p((1 << 20) + 2), 1.0, FAKE, FAKE,
+                                  None, FAKE, 1 << 30, None) == 1           # log_w misaligned
 
 
 def _table(lib, path):

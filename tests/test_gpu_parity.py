@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import datagen
+import oracle
 from tests import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
@@ -315,3 +316,72 @@ def test_tune_and_every_config_agree(km, dtype, d, tmp_path):
     # the oracle agrees with the (shared) result
     Xd = H.decode(X.cpu(), dtype)
     H.check_assign(Xd, C.cpu().numpy(), ref[0].numpy(), ref[2], dtype, min_d2=ref[1].numpy(), tag=f"tune-{dtype}-{d}")
+
+
+def _mixture(n, d, k, dtype, seed, batch=1, m=None):
+    return datagen.mixture(n, d, m or max(2, k // 2), dtype=dtype, center_dist="normal", center_scale=2.0,
+                           sigma=1.0, weights=None, workload_code=59, seed=seed, batch=batch, k=k)
+
+
+@pytest.mark.parametrize("dtype,d,n,k,batch", [("bf16", 128, 20_011, 300, 1), ("fp16", 64, 9_001, 2, 2),
+                                               ("fp32", 32, 30_000, 77, 1), ("bf16", 256, 5_003, 130, 3),
+                                               ("fp16", 16, 12_345, 513, 1)])
+def test_top2_matches_oracle(km, dtype, d, n, k, batch):
+    """Two nearest centroids per point against the oracle: the GPU's pair has
+    the true first and second smallest distances (up to the near-tie
+    tolerance), its distances are the direct distances of its labels, and
+    exact label mismatches are counted as near-ties."""
+    X, C0, _, _ = _mixture(n, d, k, dtype, seed=d + k, batch=batch)
+    lab2, d2 = km.assign_top2(X.cuda(), C0.cuda())
+    torch.cuda.synchronize()
+    lab2, d2 = lab2.cpu().numpy(), d2.cpu().numpy()
+    mism = 0
+    for b in range(batch):
+        Xd = H.decode(X[b], dtype)
+        Ch = oracle.round_to_format(C0[b].numpy().astype(np.float64), dtype)
+        lo, do = oracle.assign_top2(Xd, Ch)
+        g = lab2[b].astype(np.int64)
+        assert np.all((g >= 0) & (g < k)) and np.all(g[:, 0] != g[:, 1])
+        dg = np.stack([H.rowwise_sq_dist(Xd, Ch[g[:, j]]) for j in range(2)], axis=1)
+        tol = H.TOL_TIE * np.einsum("ij,ij->i", Xd, Xd)
+        assert np.all(np.abs(dg - do) <= tol[:, None] + 1e-30), f"top2 {dtype} D={d}: a pick is not a top-2 distance"
+        assert np.all(np.abs(d2[b] - dg) <= 1e-5 * np.maximum(dg, 1e-3 * tol[:, None] / H.TOL_TIE) + 1e-30)
+        mism += int(np.count_nonzero(g != lo))
+    H.log(f"top2 {dtype} D={d} n={n} k={k} B={batch}: {mism} label entries differ, all within near-tie tolerance")
+
+
+@pytest.mark.parametrize("dtype,d,n,k,sigma2,batch", [("bf16", 128, 20_011, 300, 2.0, 1),
+                                                      ("fp16", 64, 9_001, 5, 0.5, 2),
+                                                      ("fp32", 32, 30_000, 77, 20.0, 1),
+                                                      ("bf16", 256, 5_003, 130, 8.0, 2),
+                                                      ("fp16", 16, 12_345, 1, 1.0, 1)])
+def test_soft_assign_matches_oracle(km, dtype, d, n, k, sigma2, batch):
+    """Gaussian-mixture log density and most responsible component against
+    the oracle, with per-instance log-weights.  A score error e (distance
+    units) moves every a_k by e / (2 sigma2), so labels may differ only where
+    the two best a_k are within tol_a = 1e-5 ||x||^2 / (2 sigma2) +
+    1e-6 (1 + max|log w|); log densities agree within 2 tol_a + 1e-5 (1 + |L|)."""
+    X, C0, _, _ = _mixture(n, d, k, dtype, seed=3 * d + k, batch=batch)
+    lw = torch.randn(batch, k, generator=torch.Generator().manual_seed(k)) * 0.7
+    lab, L, tot = km.assign_soft(X.cuda(), C0.cuda(), sigma2, log_w=lw.cuda())
+    torch.cuda.synchronize()
+    lab, L, tot = lab.cpu().numpy(), L.cpu().numpy().astype(np.float64), tot.cpu().numpy()
+    near = 0
+    for b in range(batch):
+        Xd = H.decode(X[b], dtype)
+        Ch = oracle.round_to_format(C0[b].numpy().astype(np.float64), dtype)
+        lwb = lw[b].numpy().astype(np.float64)
+        lo, Lo = oracle.soft_assign(Xd, Ch, lwb, sigma2)
+        xx = np.einsum("ij,ij->i", Xd, Xd)
+        tol_a = H.TOL_TIE * xx / (2 * sigma2) + 1e-6 * (1 + np.abs(lwb).max())
+        bad = np.nonzero(lab[b] != lo)[0]
+        if bad.size:
+            A = lwb[None, :] - oracle.sq_dist_direct(Xd[bad], Ch) / (2 * sigma2)
+            gap = A[np.arange(bad.size), lo[bad]] - A[np.arange(bad.size), lab[b][bad]]
+            assert np.all(gap <= tol_a[bad]), f"soft {dtype} D={d}: label mismatch beyond near-ties"
+            near += bad.size
+        err = np.abs(L[b] - Lo)
+        lim = 2 * tol_a + 1e-5 * (1 + np.abs(Lo))
+        assert np.all(err <= lim), f"soft {dtype} D={d}: log density off by {err.max():.3e}"
+        assert abs(tot[b] - Lo.sum()) <= lim.sum(), f"soft {dtype} D={d}: total {tot[b]} vs {Lo.sum()}"
+    H.log(f"soft {dtype} D={d} n={n} k={k} s2={sigma2} B={batch}: {near} near-tie labels")
