@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="rows in the oracle timing sample")
+    ap.add_argument("--epilogue", default="argmax", choices=["argmax", "top2", "soft"],
+                    help="also time the assignment kernel with this epilogue (top-2 labels, or the Gaussian-mixture "
+                         "log density with sigma2=1) on the same workload")
     ap.add_argument("--tune", action="store_true",
                     help="time every compiled assign configuration on this shape first (kmeans_tune) and report it")
     ap.add_argument("--probe", action="store_true",
@@ -260,6 +263,25 @@ def main():
     }
     if tuning is not None:
         out["tuning"] = tuning
+    if args.epilogue != "argmax":
+        if args.epilogue == "top2":
+            def epi():
+                km.assign_top2(X, C0, ws=ws)
+        else:
+            def epi():
+                km.assign_soft(X, C0, 1.0, ws=ws)
+        for _ in range(max(1, args.warmup)):
+            epi()
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for _ in range(args.steps):
+            epi()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        e_ms = t_start.elapsed_time(t_end) / args.steps
+        e_tf = flops / (e_ms * 1e-3) / 1e12
+        out["epilogue"] = {"mode": args.epilogue, "ms": e_ms, "tflops": e_tf, "frac_mfma_peak": e_tf / peak,
+                           "time_vs_argmax_assign": e_ms / a_ms}
     if not args.no_cpu_baseline:
         # rows of the oracle's timing sample: about 10-30 s of host work each
         sample = args.cpu_sample or {"c1": 65536, "c2": 1 << 20, "c3": 1 << 17, "c4": 16384}[name]
