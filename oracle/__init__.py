@@ -28,6 +28,7 @@ from .fp64 import (  # noqa: F401
     assign,
     assign_top2,
     soft_assign,
+    gauss_sum,
     update,
     inertia,
     lloyd,

@@ -15,6 +15,10 @@ Sources, cited by page title and section:
   (paper page), abstract: Gaussian-mixture soft clustering computed in one
   pass without materialising the responsibility matrix, and border vectors
   assigned to more than one cluster.
+* [GS] "Fast Gauss Sums via Flash Attention" (paper page), abstract: Gauss
+  kernel sums with arbitrary signed weights; and the FlashDiffusion card on
+  the same listing, abstract: dense Gaussian kernel blocks evaluated in
+  fused tiles without the N x N matrix.
 
 Readings taken where the pages are silent (each is also listed in the design
 notes):
@@ -207,6 +211,25 @@ def soft_assign(X, Chat, log_w, sigma2: float):
         lab[r0:r0 + rows] = A.argmax(axis=1)          # first maximum: lowest index
         L[r0:r0 + rows] = m + np.log(np.exp(A - m[:, None]).sum(axis=1))
     return lab, L
+
+
+def gauss_sum(X, Y, w, sigma2: float):
+    """Gauss kernel sum at every point: G_i = sum_k w_k exp(-||x_i - y_k||^2 / (2 sigma2)),
+    weights of any sign, squared distance the direct fp64 sum.  [GS] abstract
+    (Gauss sums with signed weights; matrix-free Gaussian kernel blocks).
+    Reading: the bandwidth enters as 2 * sigma2 (the pages fix no convention);
+    the sources are given already rounded to the dtype of X, as centroids are.
+    Returns G fp64 [n]."""
+    X = np.asarray(X, np.float64)
+    Y = np.asarray(Y, np.float64)
+    w = np.asarray(w, np.float64)
+    n = X.shape[0]
+    G = np.empty(n)
+    rows = max(1, (1 << 22) // max(1, Y.shape[0] * Y.shape[1]))
+    for r0 in range(0, n, rows):
+        # rounded products, then their sum (no fused multiply-add: w e - w e is exactly 0)
+        G[r0:r0 + rows] = (np.exp(-sq_dist_direct(X[r0:r0 + rows], Y) / (2.0 * sigma2)) * w[None, :]).sum(axis=1)
+    return G
 
 
 def update(X, labels, C_prev, k: int):

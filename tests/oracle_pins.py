@@ -412,3 +412,35 @@ def pin_soft(L):
 
 
 ALL_PINS += [pin_top2, pin_soft]
+
+
+def pin_gauss(L):
+    """Signed-weight Gauss sums: closed forms, cancellation, linearity, the
+    wide-kernel limit, and agreement with the pinned soft assignment."""
+    # one source: G = w exp(-d / (2 s2))
+    for s2, w0, x in ((0.5, 2.5, [3.0, 4.0]), (4.0, -1.5, [1.0, -2.0])):
+        G = L.gauss_sum(np.array([x]), np.zeros((1, 2)), np.array([w0]), s2)
+        d = x[0] ** 2 + x[1] ** 2
+        assert abs(G[0] - w0 * np.exp(-d / (2 * s2))) <= 1e-15 * abs(w0)
+    # two identical sources with opposite weights cancel exactly
+    G = L.gauss_sum(np.array([[0.3, -0.7], [2.0, 1.0]]), np.array([[1.0, 1.0], [1.0, 1.0]]), np.array([1.75, -1.75]),
+                    1.3)
+    assert np.all(G == 0.0)
+    rng = np.random.default_rng(8)
+    X = rng.normal(size=(300, 8))
+    Y = rng.normal(size=(40, 8)) * 1.5
+    w1, w2 = rng.normal(size=40), rng.normal(size=40)
+    # linear in the weights; the order of the sources does not matter
+    G1, G2 = L.gauss_sum(X, Y, w1, 2.0), L.gauss_sum(X, Y, w2, 2.0)
+    assert np.allclose(L.gauss_sum(X, Y, 3.0 * w1 - 0.5 * w2, 2.0), 3.0 * G1 - 0.5 * G2, rtol=1e-12, atol=1e-12)
+    perm = rng.permutation(40)
+    assert np.allclose(L.gauss_sum(X, Y[perm], w1[perm], 2.0), G1, rtol=1e-12, atol=1e-14)
+    # a very wide kernel sums the weights
+    assert np.allclose(L.gauss_sum(X, Y, w1, 1e14), w1.sum(), rtol=1e-9, atol=1e-9)
+    # positive weights: log G is the (pinned) mixture log density with log-weights log w
+    wp = np.abs(w1) + 0.1
+    _, Ls = L.soft_assign(X, Y, np.log(wp), 0.7)
+    assert np.allclose(np.log(L.gauss_sum(X, Y, wp, 0.7)), Ls, rtol=0, atol=1e-10)
+
+
+ALL_PINS.append(pin_gauss)

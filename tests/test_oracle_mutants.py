@@ -158,7 +158,32 @@ def _soft_mode_last(X, Chat, log_w, sigma2):
     return k - 1 - A[:, ::-1].argmax(axis=1), Lx                    # ties to the highest index
 
 
+_real_gauss = L.gauss_sum
+
+
+def _gauss_no_half(X, Y, w, sigma2):
+    return _real_gauss(X, Y, w, sigma2 / 2.0)                       # exp(-d / s2)
+
+
+def _gauss_unweighted(X, Y, w, sigma2):
+    return _real_gauss(X, Y, np.ones_like(np.asarray(w, np.float64)), sigma2)
+
+
+def _gauss_sign(X, Y, w, sigma2):
+    Dm = L.sq_dist_direct(X, Y)
+    with np.errstate(over="ignore"):
+        return np.exp(Dm / (2.0 * sigma2)) @ np.asarray(w, np.float64)   # wrong sign in the exponent
+
+
+def _gauss_weight_shift(X, Y, w, sigma2):
+    return _real_gauss(X, Y, np.roll(np.asarray(w, np.float64), 1), sigma2)   # weights off by one source
+
+
 MUTANTS = {
+    "gauss_no_half": ("gauss_sum", _gauss_no_half),
+    "gauss_unweighted": ("gauss_sum", _gauss_unweighted),
+    "gauss_sign": ("gauss_sum", _gauss_sign),
+    "gauss_weight_shift": ("gauss_sum", _gauss_weight_shift),
     "top2_high_tie": ("assign_top2", _top2_high_tie),
     "top2_second_is_third": ("assign_top2", _top2_second_is_third),
     "soft_no_shift": ("soft_assign", _soft_no_shift),
