@@ -2,7 +2,7 @@
 
 Each ``csrc/*.hip`` source compiles to an object in parallel under
 ``_build/``; the objects link into ``libflashkm.so`` next to this file.
-Usage: ``python -m exact_means_clustering_amd.build`` (or ``build()``).
+Usage: ``python exact_means_clustering_amd/build.py`` (or ``build()``).
 """
 
 from __future__ import annotations

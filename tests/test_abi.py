@@ -15,8 +15,8 @@ LIB = os.path.join(ROOT, "exact_means_clustering_amd", "libflashkm.so")
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from exact_means_clustering_amd.build import build
-        build()
+        import __graft_entry__
+        __graft_entry__.build()
     return ctypes.CDLL(LIB)
 
 
@@ -29,7 +29,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {
         "kmeans_workspace_bytes", "kmeans_assign", "kmeans_update", "kmeans_fit", "kmeans_fit_streamed",
-        "kmeans_assign_top2", "kmeans_assign_soft", "kmeans_tune", "kmeans_tune_save", "kmeans_tune_load",
+        "kmeans_assign_top2", "kmeans_assign_soft", "kmeans_gauss_sum", "kmeans_tune", "kmeans_tune_save", "kmeans_tune_load",
         "kmeans_last_error"}
 
 
@@ -49,6 +49,7 @@ def _sig(lib):
     lib.kmeans_tune.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, sz, P, P, P, P]
     lib.kmeans_assign_top2.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, sz, P]
     lib.kmeans_assign_soft.argtypes = [P, i32, i64, i32, i32, P, i32, P, ctypes.c_float, P, P, P, P, sz, P]
+    lib.kmeans_gauss_sum.argtypes = [P, i32, i64, i32, i32, P, i32, P, ctypes.c_float, P, P, P, sz, P]
     lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
     lib.kmeans_tune_load.argtypes = [ctypes.c_char_p]
     lib.kmeans_last_error.restype = ctypes.c_char_p
@@ -114,6 +115,9 @@ def test_validation_codes(lib):
                                   None) == 1
     assert lib.kmeans_assign_soft(FAKE, 2, 100, 128, 1, FAKE, 5, ctypes.c_void_p((1 << 20) + 2), 1.0, FAKE, FAKE,
                                   None, FAKE, 1 << 30, None) == 1           # log_w misaligned
+    assert lib.kmeans_gauss_sum(FAKE, 2, 100, 128, 1, FAKE, 5, None, 1.0, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert lib.kmeans_gauss_sum(FAKE, 2, 100, 128, 1, FAKE, 5, FAKE, -2.0, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert lib.kmeans_gauss_sum(FAKE, 2, 100, 128, 1, FAKE, 5, FAKE, 1.0, FAKE, None, FAKE, 16, None) == 3
 
 
 def _table(lib, path):
