@@ -42,9 +42,10 @@ def parse():
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="rows in the oracle timing sample")
-    ap.add_argument("--epilogue", default="argmax", choices=["argmax", "top2", "soft"],
-                    help="also time the assignment kernel with this epilogue (top-2 labels, or the Gaussian-mixture "
-                         "log density with sigma2=1) on the same workload")
+    ap.add_argument("--epilogue", default="argmax", choices=["argmax", "top2", "soft", "gauss"],
+                    help="also time the assignment kernel with this epilogue (top-2 labels, the Gaussian-mixture "
+                         "log density with sigma2=1, or signed Gauss sums over the centroids with sigma2=1) on the "
+                         "same workload")
     ap.add_argument("--tune", action="store_true",
                     help="time every compiled assign configuration on this shape first (kmeans_tune) and report it")
     ap.add_argument("--probe", action="store_true",
@@ -267,9 +268,14 @@ def main():
         if args.epilogue == "top2":
             def epi():
                 km.assign_top2(X, C0, ws=ws)
-        else:
+        elif args.epilogue == "soft":
             def epi():
                 km.assign_soft(X, C0, 1.0, ws=ws)
+        else:
+            gw = torch.randn(C0.shape[:-1], generator=torch.Generator().manual_seed(1)).to(dev)
+
+            def epi():
+                km.gauss_sum(X, C0, gw, 1.0, ws=ws)
         for _ in range(max(1, args.warmup)):
             epi()
         torch.cuda.synchronize()

@@ -18,8 +18,8 @@ import os
 
 import torch
 
-__all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "assign_top2", "assign_soft", "update", "fit",
-           "fit_streamed", "tune", "tune_save", "tune_load", "DTYPES"]
+__all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "assign_top2", "assign_soft", "gauss_sum", "update",
+           "fit", "fit_streamed", "tune", "tune_save", "tune_load", "DTYPES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libflashkm.so"
@@ -41,7 +41,7 @@ def lib_path() -> str:
 def _load(path=None):
     path = path or lib_path()
     if not os.path.exists(path):
-        raise ImportError(f"{path} is not built: run `python -m exact_means_clustering_amd.build` "
+        raise ImportError(f"{path} is not built: run `python exact_means_clustering_amd/build.py` "
                           "(there is no CPU fallback)")
     lib = ctypes.CDLL(path)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -59,6 +59,8 @@ def _load(path=None):
     lib.kmeans_assign_top2.restype = ctypes.c_int
     lib.kmeans_assign_soft.argtypes = [P, i32, i64, i32, i32, P, i32, P, ctypes.c_float, P, P, P, P, sz, P]
     lib.kmeans_assign_soft.restype = ctypes.c_int
+    lib.kmeans_gauss_sum.argtypes = [P, i32, i64, i32, i32, P, i32, P, ctypes.c_float, P, P, P, sz, P]
+    lib.kmeans_gauss_sum.restype = ctypes.c_int
     lib.kmeans_tune.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, sz, P, P, P, P]
     lib.kmeans_tune.restype = ctypes.c_int
     lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
@@ -175,6 +177,22 @@ def assign_soft(X, C, sigma2: float, *, log_w=None, ws=None, stream=None):
     _check(_lib.kmeans_assign_soft(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(log_w), float(sigma2), _ptr(labels),
                                    _ptr(logp), _ptr(total), _ptr(ws), ws.numel(), _stream(stream)))
     return labels, logp, total
+
+
+def gauss_sum(X, Y, w, sigma2: float, *, ws=None, stream=None):
+    """Gauss kernel sums G[.., i] = sum_k w[.., k] exp(-||x_i - y_k||^2 / (2 sigma2)): returns (G fp32, sum fp64 [B])."""
+    _need(X, "X")
+    _need(Y, "Y", torch.float32)
+    _need(w, "w", torch.float32)
+    B, N, D = _shape3(X)
+    K = Y.shape[-2]
+    dt = _dtype(X)
+    G = torch.empty(X.shape[:-1], dtype=torch.float32, device=X.device)
+    total = torch.empty(B, dtype=torch.float64, device=X.device)
+    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    _check(_lib.kmeans_gauss_sum(_ptr(X), dt, N, D, B, _ptr(Y), K, _ptr(w), float(sigma2), _ptr(G), _ptr(total),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
+    return G, total
 
 
 def update(X, labels, C_prev, *, C_new=None, ws=None, stream=None):

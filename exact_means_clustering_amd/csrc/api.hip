@@ -230,6 +230,33 @@ int kmeans_assign_soft(const void* X, int32_t dtype, int64_t N, int32_t D, int32
   return KM_OK;
 }
 
+int kmeans_gauss_sum(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const float* Y, int32_t K,
+                     const float* w, float sigma2, float* gsum, double* total, void* ws, size_t ws_bytes,
+                     void* stream) {
+  err_buf()[0] = 0;
+  if (int rc = check_shape(dtype, N, D, K, B)) return rc;
+  if (!(sigma2 > 0.f) || !(sigma2 < INFINITY)) return fail(KM_EINVAL, "sigma2 must be positive and finite");
+  if (!X || !Y || !w || !gsum) return fail(KM_EINVAL, "X, Y, w and gsum must be non-null");
+  if (!aligned(X, 16) || !aligned(Y, 4) || !aligned(w, 4) || !aligned(gsum, 4) || !aligned(total, 8))
+    return fail(KM_EINVAL, "misaligned pointer (X needs 16 bytes)");
+  const Layout L = make_layout(N, D, K, B, dtype);
+  if (int rc = check_ws(ws, ws_bytes, L)) return rc;
+  Work wk = carve(ws, L);
+  hipStream_t s = (hipStream_t)stream;
+  KM_HIP(launch_prep(dtype, D, Y, wk.chat, wk.hb, B, K, s), "source prep launch");
+  KM_HIP(launch_pad_weights(w, wk.wpad, B, K, s), "weight pad launch");
+  // labels of the nearest source go to the workspace's counts region (B*K >= B*N is not
+  // guaranteed, so they use the sort buffers, which hold 2*B*N words)
+  int32_t* lab = reinterpret_cast<int32_t*>(wk.sort.kv[0]);
+  const SoftArgs sa{nullptr, 1.4426950408889634f / sigma2, 0.5f / sigma2, wk.wpad};
+  KM_HIP(launch_assign_gauss(dtype, D, X, wk.chat, wk.hb, N, K, B, lab, gsum, wk.part, sa, s), "gauss sum launch");
+  if (total) {
+    const int64_t nwg = (N + mode_config(dtype, D).rows() - 1) / mode_config(dtype, D).rows();
+    KM_HIP(launch_inertia_reduce(wk.part, (int)nwg, B, total, nullptr, false, s), "total launch");
+  }
+  return KM_OK;
+}
+
 int kmeans_tune(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const float* C, int32_t K,
                 int32_t* labels, void* ws, size_t ws_bytes, void* stream, int32_t* pb, int32_t* waves, float* ms) {
   err_buf()[0] = 0;

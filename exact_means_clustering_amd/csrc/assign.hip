@@ -163,8 +163,13 @@ __device__ __forceinline__ void improve(const f32x16& acc, float tmax, float& be
 //            sigma2 * log w_k): the best score and index plus the running
 //            sum l = sum_k 2^(t_k - t_best) with t_k = score_k * log2(e) / sigma2;
 //            labels = most responsible component, dist = log density, part =
-//            per-workgroup sums of it.
-enum AssignMode : int { kArgmax = 0, kTop2 = 1, kSoft = 2 };
+//            per-workgroup sums of it;
+//   kGauss   the same running maximum, and the signed sum
+//            sum_k w_k 2^(t_k - t_best) (weights from the padded array
+//            soft.wpad, staged in LDS with the tile): dist = the Gauss sum
+//            sum_k w_k exp(-||x - c_k||^2 / (2 sigma2)), part = its sums,
+//            labels = the nearest source.
+enum AssignMode : int { kArgmax = 0, kTop2 = 1, kSoft = 2, kGauss = 3 };
 
 template <class T, int D, int PB, int W, int MODE>
 __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* __restrict__ X,
@@ -177,6 +182,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
   constexpr int TK = Cfg::TK;
   __shared__ uint4 tile[2][Cfg::TILE_CH];
   __shared__ __align__(16) float tb[2][TK];  // read back as float4
+  __shared__ __align__(16) float tw[MODE == kGauss ? 2 : 1][MODE == kGauss ? TK : 4];  // kGauss: weights
   __shared__ double wsum[W];
 
   const int tid = threadIdx.x;
@@ -232,6 +238,13 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
         const float4* src = reinterpret_cast<const float4*>(hbb + (int64_t)t * TK) + lane;
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&tb[buf][0], 16, 0, 0);
       }
+      if constexpr (MODE == kGauss) {
+        // the weights of the tile's centroids (zero-padded like the bias)
+        if (w == W - 2 && lane < TK / 4) {
+          const float4* src = reinterpret_cast<const float4*>(soft.wpad + (int64_t)b * kpad(K) + (int64_t)t * TK) + lane;
+          __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&tw[buf][0], 16, 0, 0);
+        }
+      }
     };
     // all of this wave's LDS loads have landed (then a barrier publishes them)
     auto wait_tile = [] { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ };
@@ -282,7 +295,17 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
         bias[4 * q + 3] = bq.w;
       }
     };
-    auto reduce_group = [&](const f32x16 (&a)[G][PB], int base) {
+    auto read_weights = [&](int buf, int sb, f32x16& wv) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 wq = *reinterpret_cast<const float4*>(&tw[MODE == kGauss ? buf : 0][sb * 32 + 8 * q + 4 * h]);
+        wv[4 * q + 0] = wq.x;
+        wv[4 * q + 1] = wq.y;
+        wv[4 * q + 2] = wq.z;
+        wv[4 * q + 3] = wq.w;
+      }
+    };
+    auto reduce_group = [&](const f32x16 (&a)[G][PB], int base, const f32x16 (&wv)[G]) {
       float tmax[G][PB];
       bool any = false;
 #pragma unroll
@@ -292,7 +315,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
           tmax[j][p] = max16(a[j][p]);
           any |= tmax[j][p] > (MODE == kTop2 ? sec[p] : best[p]);
         }
-      if constexpr (MODE == kSoft) {
+      if constexpr (MODE == kSoft || MODE == kGauss) {
         // rescale the running sum to the new maximum, then add this group's
         // terms (a group of padding rows, all -inf, changes nothing)
 #pragma unroll
@@ -304,7 +327,11 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
             const float m2 = mb * soft.scale2;
             float sum = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(a[j][p][r], soft.scale2, -m2));
+            for (int r = 0; r < 16; ++r) {
+              const float e = __builtin_amdgcn_exp2f(fmaf(a[j][p][r], soft.scale2, -m2));
+              if constexpr (MODE == kGauss) sum = fmaf(wv[j][r], e, sum);
+              else sum += e;
+            }
             lsum[p] = lsum[p] * __builtin_amdgcn_exp2f(best[p] * soft.scale2 - m2) + sum;
           }
       }
@@ -323,6 +350,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
     };
 
     f32x16 prev[G][PB];
+    f32x16 wprev[G];  // kGauss: the weights of the delayed group
     int prev_base = 0;
     if constexpr (Cfg::DELAY) {
 #pragma unroll
@@ -331,6 +359,10 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
         for (int p = 0; p < PB; ++p)
 #pragma unroll
           for (int r = 0; r < 16; ++r) prev[j][p][r] = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) wprev[j][r] = 0.f;
     }
 
     for (int t = 0; t < ntiles; ++t) {
@@ -359,12 +391,14 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
           for (int j = 0; j < G; ++j) read_frag(buf, g * G + j, af[j]);
         }
         f32x16 acc[G][PB];
+        f32x16 wv[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           f32x16 bias;
           read_bias(buf, g * G + j, bias);
 #pragma unroll
           for (int p = 0; p < PB; ++p) acc[j][p] = bias;
+          if constexpr (MODE == kGauss) read_weights(buf, g * G + j, wv[j]);
         }
 #pragma unroll
         for (int st = 0; st < STEPS; ++st)
@@ -374,7 +408,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
             for (int p = 0; p < PB; ++p) acc[j][p] = Mfma<T>::step(af[j], xf[p], st, acc[j][p]);
         const int base = t * TK + g * G * 32 + 4 * h;
         if constexpr (Cfg::DELAY) {
-          reduce_group(prev, prev_base);
+          reduce_group(prev, prev_base, wprev);
 #pragma unroll
           for (int i = 0; i < STEPS * PB * G; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -384,15 +418,19 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
           for (int j = 0; j < G; ++j)
 #pragma unroll
             for (int p = 0; p < PB; ++p) prev[j][p] = acc[j][p];
+          if constexpr (MODE == kGauss) {
+#pragma unroll
+            for (int j = 0; j < G; ++j) wprev[j] = wv[j];
+          }
           prev_base = base;
         } else {
-          reduce_group(acc, base);
+          reduce_group(acc, base, wv);
         }
       }
       wait_tile();
       __syncthreads();
     }
-    if constexpr (Cfg::DELAY) reduce_group(prev, prev_base);
+    if constexpr (Cfg::DELAY) reduce_group(prev, prev_base, wprev);
 
     // squared distance of point block p to centroid k, computed directly (no
     // cancellation): each lane half sums its dims, the halves then add.
@@ -447,7 +485,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
         }
       } else {
         float l = 0.f;
-        if constexpr (MODE == kSoft) {
+        if constexpr (MODE == kSoft || MODE == kGauss) {
           // combine the halves' sums at the larger maximum
           const float ol = __shfl_xor(lsum[p], 32);
           const float m2 = (ob > best[p] ? ob : best[p]) * soft.scale2;
@@ -468,6 +506,11 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
             const float L = lw - d2 * soft.inv2s2 + __builtin_amdgcn_logf(l) * 0.693147180559945309f;
             min_d2[(int64_t)b * N + n] = L;
             wacc += (double)L;
+          } else if constexpr (MODE == kGauss) {
+            // sum_k w_k exp(-d_k / (2 sigma2)) = exp(-d_best / (2 sigma2)) * sum_k w_k 2^(t_k - t_best)
+            const float Gs = l * __builtin_amdgcn_exp2f(-d2 * soft.inv2s2 * 1.44269504088896341f);
+            min_d2[(int64_t)b * N + n] = Gs;
+            wacc += (double)Gs;
           } else {
             if (min_d2) min_d2[(int64_t)b * N + n] = d2;
             wacc += (double)d2;
@@ -658,6 +701,7 @@ template <class T, int D> struct AssignF {
       case kArgmax: return assign_cfg<T, D, kArgmax>(c, X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
       case kTop2: return assign_cfg<T, D, kTop2>(c, X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
       case kSoft: return assign_cfg<T, D, kSoft>(c, X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
+      case kGauss: return assign_cfg<T, D, kGauss>(c, X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -731,6 +775,29 @@ hipError_t launch_assign_soft(int dt, int D, const void* X, const void* Chat, co
                               int32_t* labels, float* logp, double* part, SoftArgs soft, hipStream_t s) {
   return dispatch_dt_d<AssignF>(dt, D, (int)kSoft, mode_config(dt, D), X, Chat, hb, N, K, B, labels, logp, part,
                                 soft, s);
+}
+
+hipError_t launch_assign_gauss(int dt, int D, const void* X, const void* Chat, const float* hb, int64_t N, int K,
+                               int B, int32_t* labels, float* gsum, double* part, SoftArgs soft, hipStream_t s) {
+  return dispatch_dt_d<AssignF>(dt, D, (int)kGauss, mode_config(dt, D), X, Chat, hb, N, K, B, labels, gsum, part,
+                                soft, s);
+}
+
+namespace {
+__global__ __launch_bounds__(256) void pad_weights_kernel(const float* __restrict__ w, float* __restrict__ wpad,
+                                                          int64_t B, int K, int Kp) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * Kp) return;
+  const int64_t b = i / Kp;
+  const int k = (int)(i - b * Kp);
+  wpad[i] = k < K ? w[b * K + k] : 0.f;
+}
+}  // namespace
+
+hipError_t launch_pad_weights(const float* w, float* wpad, int64_t B, int K, hipStream_t s) {
+  const int64_t n = B * kpad(K);
+  pad_weights_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(w, wpad, B, K, (int)kpad(K));
+  return hipGetLastError();
 }
 
 hipError_t assign_prime(int dt, int D, AssignConfig cfg) { return dispatch_dt_d<PrimeF>(dt, D, cfg); }

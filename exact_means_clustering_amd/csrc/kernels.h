@@ -60,9 +60,17 @@ struct SoftArgs {
   const float* log_w;  // [B,K] or null (all zero)
   float scale2;        // log2(e) / sigma2
   float inv2s2;        // 1 / (2 sigma2)
+  const float* wpad;   // Gauss sums: weights [B, kpad(K)], zero past K
 };
 hipError_t launch_assign_soft(int dt, int D, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
                               int32_t* labels, float* logp, double* part, SoftArgs soft, hipStream_t s);
+// Gauss kernel sums gsum[b,i] = sum_k w_k exp(-||x - c_k||^2 / (2 sigma2)) (bias
+// from launch_prep without log-weights; soft.wpad from launch_pad_weights);
+// labels = nearest source, part = per-workgroup sums.
+hipError_t launch_assign_gauss(int dt, int D, const void* X, const void* Chat, const float* hb, int64_t N, int K,
+                               int B, int32_t* labels, float* gsum, double* part, SoftArgs soft, hipStream_t s);
+// wpad[b * kpad(K) + k] = w[b * K + k] for k < K, 0 beyond.
+hipError_t launch_pad_weights(const float* w, float* wpad, int64_t B, int K, hipStream_t s);
 // Configuration of the top-2 and soft launches (rows per workgroup: rows()).
 AssignConfig mode_config(int dt, int D);
 

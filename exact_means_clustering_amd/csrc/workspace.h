@@ -26,7 +26,7 @@ inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Byte offsets of the scratch regions inside one workspace, 256-byte aligned.
 struct Layout {
-  size_t chat, hb, part, cnt, kv0, kv1, hist, dtot, off, frag, gfrag, total;
+  size_t chat, hb, wpad, part, cnt, kv0, kv1, hist, dtot, off, frag, gfrag, total;
 };
 
 inline Layout make_layout(int64_t N, int D, int K, int B, int dt) {
@@ -36,6 +36,7 @@ inline Layout make_layout(int64_t N, int D, int K, int B, int dt) {
   size_t o = 0;
   L.chat = o;  o = al256(o + (size_t)nseg * D * dtype_size(dt));
   L.hb = o;    o = al256(o + (size_t)B * kpad(K) * 4);
+  L.wpad = o;  o = al256(o + (size_t)B * kpad(K) * 4);
   L.part = o;  o = al256(o + (size_t)B * assign_max_wgs(N) * 8);
   L.cnt = o;   o = al256(o + (size_t)nseg * 4);
   L.kv0 = o;   o = al256(o + (size_t)n * 8);
@@ -52,6 +53,7 @@ inline Layout make_layout(int64_t N, int D, int K, int B, int dt) {
 struct Work {
   void* chat;
   float* hb;
+  float* wpad;
   double* part;
   int32_t* cnt;
   SortBuffers sort;
@@ -64,6 +66,7 @@ inline Work carve(void* ws, const Layout& L) {
   Work w;
   w.chat = at(L.chat);
   w.hb = reinterpret_cast<float*>(at(L.hb));
+  w.wpad = reinterpret_cast<float*>(at(L.wpad));
   w.part = reinterpret_cast<double*>(at(L.part));
   w.cnt = reinterpret_cast<int32_t*>(at(L.cnt));
   w.sort.kv[0] = reinterpret_cast<uint2*>(at(L.kv0));

@@ -169,6 +169,22 @@ KM_API int kmeans_assign_soft(const void* X, int32_t dtype, int64_t N, int32_t D
                               int32_t* labels, float* log_density, double* total,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* Gauss kernel sums with the same fused tile ("Fast Gauss Sums via Flash
+ * Attention" page, abstract: Gaussian kernel sums with arbitrary signed
+ * weights; the FlashDiffusion card on the same listing, abstract: dense
+ * Gaussian kernel blocks evaluated in fused tiles, never materialised).
+ *   gsum[b,i] = sum_k w[b,k] exp(-||x_bi - y_bk||^2 / (2 sigma2))   (fp32)
+ *   total[b]  = sum_i gsum[b,i] in fp64 (nullable)
+ * X [B,N,D] dtype (targets), Y [B,K,D] fp32 sources rounded to dtype like
+ * centroids, w [B,K] fp32 weights of any sign, sigma2 > 0; K <= N as for the
+ * assignment.  The kernel keeps a running maximum score and the signed sum
+ * sum_k w_k 2^(t_k - t_max) per target, anchored on the direct distance of
+ * the nearest source.  Asynchronous. */
+KM_API int kmeans_gauss_sum(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
+                            const float* Y, int32_t K, const float* w, float sigma2,
+                            float* gsum, double* total,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Shape-keyed configuration of the assignment kernel, with a per-shape
  * tuning cache (the pages' point about configuration tuning under dynamic
  * shapes: paper page abstract and the article section "Flash-KMeans が変える

@@ -385,3 +385,34 @@ def test_soft_assign_matches_oracle(km, dtype, d, n, k, sigma2, batch):
         assert np.all(err <= lim), f"soft {dtype} D={d}: log density off by {err.max():.3e}"
         assert abs(tot[b] - Lo.sum()) <= lim.sum(), f"soft {dtype} D={d}: total {tot[b]} vs {Lo.sum()}"
     H.log(f"soft {dtype} D={d} n={n} k={k} s2={sigma2} B={batch}: {near} near-tie labels")
+
+
+@pytest.mark.parametrize("dtype,d,n,k,sigma2,batch", [("bf16", 128, 20_011, 300, 100.0, 1),
+                                                      ("fp16", 64, 9_001, 33, 50.0, 2),
+                                                      ("fp32", 32, 30_000, 77, 20.0, 1),
+                                                      ("bf16", 256, 5_003, 130, 200.0, 2),
+                                                      ("fp16", 16, 12_345, 1, 10.0, 1)])
+def test_gauss_sum_matches_oracle(km, dtype, d, n, k, sigma2, batch):
+    """Signed-weight Gauss sums against the oracle.  A score error e moves each
+    term's exponent by e / (2 sigma2), so the error bound is relative to
+    S_i = sum_k |w_k| exp(-d_ik / (2 sigma2)): (tol_a + 5e-6) S_i with
+    tol_a = 1e-5 ||x||^2 / (2 sigma2), plus 1e-30 sum|w| for fp32 underflow."""
+    X, Y, _, _ = _mixture(n, d, k, dtype, seed=5 * d + k, batch=batch)
+    w = torch.randn(batch, k, generator=torch.Generator().manual_seed(d + k))
+    G, tot = km.gauss_sum(X.cuda(), Y.cuda(), w.cuda(), sigma2)
+    torch.cuda.synchronize()
+    G, tot = G.cpu().numpy().astype(np.float64), tot.cpu().numpy()
+    worst = 0.0
+    for b in range(batch):
+        Xd = H.decode(X[b], dtype)
+        Yh = oracle.round_to_format(Y[b].numpy().astype(np.float64), dtype)
+        wb = w[b].numpy().astype(np.float64)
+        Go = oracle.gauss_sum(Xd, Yh, wb, sigma2)
+        S = oracle.gauss_sum(Xd, Yh, np.abs(wb), sigma2)
+        tol_a = H.TOL_TIE * np.einsum("ij,ij->i", Xd, Xd) / (2 * sigma2)
+        lim = (tol_a + 5e-6) * S + 1e-30 * np.abs(wb).sum()
+        err = np.abs(G[b] - Go)
+        assert np.all(err <= lim), f"gauss {dtype} D={d}: error {err.max():.3e} vs bound {lim[err.argmax()]:.3e}"
+        assert abs(tot[b] - Go.sum()) <= lim.sum(), f"gauss {dtype} D={d}: total {tot[b]} vs {Go.sum()}"
+        worst = max(worst, float(np.max(err / np.maximum(S, 1e-300))))
+    H.log(f"gauss {dtype} D={d} n={n} k={k} s2={sigma2} B={batch}: max error / S = {worst:.1e}")
