@@ -29,6 +29,8 @@ from .fp64 import (  # noqa: F401
     assign_top2,
     soft_assign,
     gauss_sum,
+    seed_random,
+    kmeanspp,
     update,
     inertia,
     lloyd,

@@ -232,6 +232,41 @@ def gauss_sum(X, Y, w, sigma2: float):
     return G
 
 
+def seed_random(n: int, u) -> np.ndarray:
+    """Random seeding: centroid j is row floor(u_j * n) (with replacement), u_j
+    uniforms in [0, 1) supplied by the caller.  The pages only name seeding as
+    outside the method's inner loop ([HN] なぜ Hacker News のスレッドが重要だったか);
+    this is the plainest random initialisation.  Returns int64 [k]."""
+    u = np.asarray(u, np.float64)
+    return np.minimum(np.floor(u * n).astype(np.int64), n - 1)
+
+
+def kmeanspp(X, u) -> tuple[np.ndarray, np.ndarray]:
+    """k-means++ (D^2) seeding, the seeding named in [HN] なぜ Hacker News の
+    スレッドが重要だったか, with the caller's uniforms u [k]:
+      c_0 = row floor(u_0 * n);
+      for j >= 1: D2_i = min over the chosen rows c of ||x_i - c||^2 (direct
+      fp64), and c_j = row i for the smallest i with
+      sum_{i' <= i} D2_i' > u_j * sum_i D2_i  (the inverse CDF of D^2 sampling);
+      if sum_i D2_i = 0 (every row coincides with a chosen one), row floor(u_j * n).
+    Returns (chosen rows int64 [k], D2 after the last choice fp64 [n])."""
+    X = np.asarray(X, np.float64)
+    u = np.asarray(u, np.float64)
+    n = X.shape[0]
+    idx = np.empty(u.shape[0], dtype=np.int64)
+    idx[0] = min(int(np.floor(u[0] * n)), n - 1)
+    d2 = _rowwise_sq_dist(X, X[idx[0]][None, :])
+    for j in range(1, u.shape[0]):
+        cum = np.cumsum(d2)
+        total = cum[-1]
+        if total > 0:
+            idx[j] = min(int(np.searchsorted(cum, u[j] * total, side="right")), n - 1)
+        else:
+            idx[j] = min(int(np.floor(u[j] * n)), n - 1)
+        d2 = np.minimum(d2, _rowwise_sq_dist(X, X[idx[j]][None, :]))
+    return idx, d2
+
+
 def update(X, labels, C_prev, k: int):
     """Centroid update stage: c_k = (1/n_k) * sum_{i: label_i = k} x_i, and an
     empty cluster keeps its previous centroid.

@@ -444,3 +444,44 @@ def pin_gauss(L):
 
 
 ALL_PINS.append(pin_gauss)
+
+
+def pin_seeding(L):
+    """k-means++ on hand-computed 1-D cases (including the boundary of the
+    inverse CDF), invariants, the degenerate all-identical case, and D^2
+    sampling frequencies."""
+    X = np.array([[0.0], [1.0], [3.0], [7.0]])          # from row 0: D2 = 0, 1, 9, 49 (cumsum 0, 1, 10, 59)
+    for u1, want in ((0.5, 3), (0.01, 1), (10.0 / 59.0 - 1e-12, 2), (10.0 / 59.0 + 1e-12, 3), (0.999, 3)):
+        idx, _ = L.kmeanspp(X, [0.0, u1])
+        assert idx.tolist() == [0, want], (u1, idx)
+    # targets exactly on a cumulative sum (dyadic total): the pick is the next row
+    Z = np.array([[0.0, 0.0, 0.0], [1.0, 0.0, 0.0], [1.0, 1.0, 1.0], [2.0, 0.0, 0.0]])   # D2 0, 1, 3, 4; cumsum 0, 1, 4, 8
+    assert L.kmeanspp(Z, [0.0, 0.5])[0].tolist() == [0, 3]      # target 4 = cumsum[2]
+    assert L.kmeanspp(Z, [0.0, 0.125])[0].tolist() == [0, 2]    # target 1 = cumsum[1]
+    assert L.kmeanspp(Z, [0.0, 0.0])[0].tolist() == [0, 1]      # target 0: the first row with D2 > 0
+    # third pick after rows 0 and 3: D2 = 0, 1, 9, 0 (cumsum 0, 1, 10, 10)
+    idx, d2 = L.kmeanspp(X, [0.0, 0.5, 0.05])
+    assert idx.tolist() == [0, 3, 1] and d2.tolist() == [0.0, 0.0, 4.0, 0.0]
+    idx, _ = L.kmeanspp(X, [0.0, 0.5, 0.5])
+    assert idx.tolist() == [0, 3, 2]
+    # first pick and random seeding: floor(u n)
+    assert L.kmeanspp(X, [0.74])[0].tolist() == [2]
+    assert L.seed_random(4, [0.0, 0.2499, 0.25, 0.999]).tolist() == [0, 0, 1, 3]
+    # all rows identical: D2 sums to 0, fall back to floor(u n)
+    idx, d2 = L.kmeanspp(np.ones((5, 3)), [0.1, 0.9, 0.3])
+    assert idx.tolist() == [0, 4, 1] and np.all(d2 == 0)
+    # no row with D2 = 0 is picked while the total is positive; final D2 is the distance to the nearest pick
+    p = datagen.make("c2", n=1500, k=20, seed=9)
+    Xd = L.decode(p.X[0].numpy(), "fp16")
+    u = np.random.default_rng(4).random(20)
+    idx, d2 = L.kmeanspp(Xd, u)
+    assert len(set(idx.tolist())) == 20
+    assert np.allclose(d2, L.sq_dist_direct(Xd, Xd[idx]).min(axis=1), rtol=1e-12, atol=0)
+    # D^2 sampling: second-pick frequencies follow D2 / sum(D2)
+    Y = np.array([[0.0], [1.0], [2.0], [4.0]])         # D2 from row 0: 0, 1, 4, 16
+    us = (np.arange(4000) + 0.5) / 4000
+    counts = np.bincount([L.kmeanspp(Y, [0.0, v])[0][1] for v in us], minlength=4)
+    assert counts.tolist() == [0, 190, 762, 3048]      # midpoints (k + 0.5) / 4000 below 1/21, 5/21, 1
+
+
+ALL_PINS.append(pin_seeding)

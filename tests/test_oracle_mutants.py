@@ -179,7 +179,58 @@ def _gauss_weight_shift(X, Y, w, sigma2):
     return _real_gauss(X, Y, np.roll(np.asarray(w, np.float64), 1), sigma2)   # weights off by one source
 
 
+_real_kpp = L.kmeanspp
+
+
+def _kpp_left(X, u):
+    X = np.asarray(X, np.float64)
+    u = np.asarray(u, np.float64)
+    n = X.shape[0]
+    idx = [min(int(np.floor(u[0] * n)), n - 1)]
+    d2 = ((X - X[idx[0]]) ** 2).sum(1)
+    for j in range(1, len(u)):
+        cum = np.cumsum(d2)
+        idx.append(min(int(np.searchsorted(cum, u[j] * cum[-1], side="left")), n - 1) if cum[-1] > 0
+                   else min(int(np.floor(u[j] * n)), n - 1))     # >= instead of >
+        d2 = np.minimum(d2, ((X - X[idx[-1]]) ** 2).sum(1))
+    return np.array(idx), d2
+
+
+def _kpp_dist_not_squared(X, u):
+    X = np.asarray(X, np.float64)
+    u = np.asarray(u, np.float64)
+    n = X.shape[0]
+    idx = [min(int(np.floor(u[0] * n)), n - 1)]
+    d = np.sqrt(((X - X[idx[0]]) ** 2).sum(1))
+    for j in range(1, len(u)):
+        cum = np.cumsum(d)                                          # D instead of D^2
+        idx.append(min(int(np.searchsorted(cum, u[j] * cum[-1], side="right")), n - 1) if cum[-1] > 0
+                   else min(int(np.floor(u[j] * n)), n - 1))
+        d = np.minimum(d, np.sqrt(((X - X[idx[-1]]) ** 2).sum(1)))
+    return np.array(idx), d * d
+
+
+def _kpp_first_center_only(X, u):
+    X = np.asarray(X, np.float64)
+    u = np.asarray(u, np.float64)
+    n = X.shape[0]
+    idx = [min(int(np.floor(u[0] * n)), n - 1)]
+    d2 = ((X - X[idx[0]]) ** 2).sum(1)
+    for j in range(1, len(u)):                                     # D2 never updated
+        cum = np.cumsum(d2)
+        idx.append(min(int(np.searchsorted(cum, u[j] * cum[-1], side="right")), n - 1))
+    return np.array(idx), d2
+
+
+def _seed_round(n, u):
+    return np.minimum(np.round(np.asarray(u, np.float64) * n).astype(np.int64), n - 1)
+
+
 MUTANTS = {
+    "kpp_left": ("kmeanspp", _kpp_left),
+    "kpp_dist_not_squared": ("kmeanspp", _kpp_dist_not_squared),
+    "kpp_first_center_only": ("kmeanspp", _kpp_first_center_only),
+    "seed_round": ("seed_random", _seed_round),
     "gauss_no_half": ("gauss_sum", _gauss_no_half),
     "gauss_unweighted": ("gauss_sum", _gauss_unweighted),
     "gauss_sign": ("gauss_sum", _gauss_sign),
