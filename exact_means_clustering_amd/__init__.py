@@ -18,7 +18,7 @@ import os
 
 import torch
 
-__all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "assign_top2", "assign_soft", "gauss_sum", "update",
+__all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "assign_top2", "assign_soft", "gauss_sum", "seed", "update",
            "fit", "fit_streamed", "tune", "tune_save", "tune_load", "DTYPES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +61,8 @@ def _load(path=None):
     lib.kmeans_assign_soft.restype = ctypes.c_int
     lib.kmeans_gauss_sum.argtypes = [P, i32, i64, i32, i32, P, i32, P, ctypes.c_float, P, P, P, sz, P]
     lib.kmeans_gauss_sum.restype = ctypes.c_int
+    lib.kmeans_seed.argtypes = [P, i32, i64, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    lib.kmeans_seed.restype = ctypes.c_int
     lib.kmeans_tune.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, sz, P, P, P, P]
     lib.kmeans_tune.restype = ctypes.c_int
     lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
@@ -193,6 +195,29 @@ def gauss_sum(X, Y, w, sigma2: float, *, ws=None, stream=None):
     _check(_lib.kmeans_gauss_sum(_ptr(X), dt, N, D, B, _ptr(Y), K, _ptr(w), float(sigma2), _ptr(G), _ptr(total),
                                  _ptr(ws), ws.numel(), _stream(stream)))
     return G, total
+
+
+def seed(X, u, *, method: str = "kmeans++", want_d2: bool = False, ws=None, stream=None):
+    """Initial centroids from the caller's uniforms u [.., K] (fp64, CUDA, in [0, 1)): method "random" (rows
+    floor(u N)) or "kmeans++" (D^2 sampling).  Returns (row indices int32 [.., K], centroids fp32 [.., K, D],
+    squared distance of every row to its nearest pick fp32 [.., N] or None)."""
+    _need(X, "X")
+    _need(u, "u", torch.float64)
+    B, N, D = _shape3(X)
+    K = u.shape[-1]
+    if u.numel() != B * K:
+        raise KMeansError(KM_EINVAL, "u must be [K] or [B, K]")
+    dt = _dtype(X)
+    m = {"random": 0, "kmeans++": 1}.get(method)
+    if m is None:
+        raise KMeansError(KM_EINVAL, f"unknown seeding method {method!r}")
+    idx = torch.empty(u.shape, dtype=torch.int32, device=X.device)
+    C = torch.empty((*u.shape, D), dtype=torch.float32, device=X.device)
+    d2 = torch.empty(X.shape[:-1], dtype=torch.float32, device=X.device) if want_d2 else None
+    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    _check(_lib.kmeans_seed(_ptr(X), dt, N, D, B, K, m, _ptr(u), _ptr(idx), _ptr(C), _ptr(d2), _ptr(ws), ws.numel(),
+                            _stream(stream)))
+    return idx, C, d2
 
 
 def update(X, labels, C_prev, *, C_new=None, ws=None, stream=None):

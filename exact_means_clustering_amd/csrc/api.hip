@@ -257,6 +257,24 @@ int kmeans_gauss_sum(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t
   return KM_OK;
 }
 
+int kmeans_seed(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, int32_t K, int32_t method,
+                const double* u, int32_t* idx, float* C, float* d2, void* ws, size_t ws_bytes, void* stream) {
+  err_buf()[0] = 0;
+  if (int rc = check_shape(dtype, N, D, K, B)) return rc;
+  if (method != 0 && method != 1) return fail(KM_EINVAL, "method must be 0 (random) or 1 (k-means++), got %d", method);
+  if (!X || !u || !idx || !C) return fail(KM_EINVAL, "X, u, idx and C must be non-null");
+  if (!aligned(X, 16) || !aligned(u, 8) || !aligned(idx, 4) || !aligned(C, 4) || !aligned(d2, 4))
+    return fail(KM_EINVAL, "misaligned pointer (X needs 16 bytes)");
+  const Layout L = make_layout(N, D, K, B, dtype);
+  if (int rc = check_ws(ws, ws_bytes, L)) return rc;
+  Work w = carve(ws, L);
+  // running D2 [B,N] fp32 in the first sort buffer (B*N*8 bytes), block sums in the partials
+  KM_HIP(launch_seed(dtype, D, X, N, B, K, method, u, idx, C, reinterpret_cast<float*>(w.sort.kv[0]), w.part, d2,
+                     (hipStream_t)stream),
+         "seeding launch");
+  return KM_OK;
+}
+
 int kmeans_tune(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const float* C, int32_t K,
                 int32_t* labels, void* ws, size_t ws_bytes, void* stream, int32_t* pb, int32_t* waves, float* ms) {
   err_buf()[0] = 0;

@@ -131,6 +131,15 @@ struct SegOut {
 hipError_t launch_segment_reduce(int dt, int D, const void* X, const uint2* sorted, int32_t* off, int64_t n,
                                  uint32_t nseg, const SegOut& out, SegBuffers& buf, hipStream_t s);
 
+// ---- seeding ------------------------------------------------------------------
+// Initial centroids of B instances: method 0 = rows floor(u N); method 1 =
+// k-means++ D^2 sampling driven by u [B,K] (fp64 uniforms in [0,1)).  idx
+// [B,K] the chosen rows, C [B,K,D] those rows in fp32.  d2_scratch [B,N]
+// fp32 and part [B, ceil(N/256)] fp64 are scratch; d2_out [B,N] (nullable)
+// receives each row's squared distance to its nearest pick.
+hipError_t launch_seed(int dt, int D, const void* X, int64_t N, int B, int K, int method, const double* u,
+                       int32_t* idx, float* C, float* d2_scratch, double* part, float* d2_out, hipStream_t s);
+
 // ---- streamed path helpers ---------------------------------------------------
 // C_new[k] = S[k] / n[k] (fp64 divide, rounded once to fp32) when n[k] > 0,
 // else C_prev[k]; counts are not produced.

@@ -185,6 +185,26 @@ KM_API int kmeans_gauss_sum(const void* X, int32_t dtype, int64_t N, int32_t D, 
                             float* gsum, double* total,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* Initial centroids on the device.  The pages name k-means++ seeding only
+ * as outside the method's inner loop (article, section なぜ Hacker News の
+ * スレッドが重要だったか); this is the standard D^2 sampling, driven by
+ * uniforms the caller draws (u [B,K] fp64 in [0,1), device):
+ *   method 0 (random):   idx[b,j] = floor(u[b,j] * N)            (with replacement)
+ *   method 1 (k-means++): idx[b,0] = floor(u[b,0] * N); for j >= 1 idx[b,j] is
+ *     the smallest row i with sum_{i'<=i} D2_bi' > u[b,j] * sum_i D2_bi, where
+ *     D2_bi is row i's squared distance to its nearest earlier pick (fp32,
+ *     computed directly; sums in fp64 in a fixed order); floor(u N) when all
+ *     D2 are zero.
+ *   C[b,j,:] = row idx[b,j] of X as fp32 (exact); d2 [B,N] fp32 (nullable)
+ *   receives every row's squared distance to its nearest pick.
+ * k-means++ is sequential in j: 2 kernel launches per pick, each streaming X
+ * once.  Arguments otherwise as kmeans_assign; asynchronous.  Deterministic;
+ * where the cumulative sum lies within rounding of u * sum, the pick may
+ * differ from an exact-arithmetic one by that rounding. */
+KM_API int kmeans_seed(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, int32_t K,
+                       int32_t method, const double* u, int32_t* idx, float* C, float* d2,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* Shape-keyed configuration of the assignment kernel, with a per-shape
  * tuning cache (the pages' point about configuration tuning under dynamic
  * shapes: paper page abstract and the article section "Flash-KMeans が変える

@@ -29,7 +29,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {
         "kmeans_workspace_bytes", "kmeans_assign", "kmeans_update", "kmeans_fit", "kmeans_fit_streamed",
-        "kmeans_assign_top2", "kmeans_assign_soft", "kmeans_gauss_sum", "kmeans_tune", "kmeans_tune_save", "kmeans_tune_load",
+        "kmeans_assign_top2", "kmeans_assign_soft", "kmeans_gauss_sum", "kmeans_seed", "kmeans_tune", "kmeans_tune_save", "kmeans_tune_load",
         "kmeans_last_error"}
 
 
@@ -50,6 +50,7 @@ def _sig(lib):
     lib.kmeans_assign_top2.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, sz, P]
     lib.kmeans_assign_soft.argtypes = [P, i32, i64, i32, i32, P, i32, P, ctypes.c_float, P, P, P, P, sz, P]
     lib.kmeans_gauss_sum.argtypes = [P, i32, i64, i32, i32, P, i32, P, ctypes.c_float, P, P, P, sz, P]
+    lib.kmeans_seed.argtypes = [P, i32, i64, i32, i32, i32, i32, P, P, P, P, P, sz, P]
     lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
     lib.kmeans_tune_load.argtypes = [ctypes.c_char_p]
     lib.kmeans_last_error.restype = ctypes.c_char_p
@@ -118,6 +119,12 @@ def test_validation_codes(lib):
     assert lib.kmeans_gauss_sum(FAKE, 2, 100, 128, 1, FAKE, 5, None, 1.0, FAKE, None, FAKE, 1 << 30, None) == 1
     assert lib.kmeans_gauss_sum(FAKE, 2, 100, 128, 1, FAKE, 5, FAKE, -2.0, FAKE, None, FAKE, 1 << 30, None) == 1
     assert lib.kmeans_gauss_sum(FAKE, 2, 100, 128, 1, FAKE, 5, FAKE, 1.0, FAKE, None, FAKE, 16, None) == 3
+    assert lib.kmeans_seed(FAKE, 2, 100, 128, 1, 5, 2, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1  # method
+    assert b"method" in lib.kmeans_last_error()
+    assert lib.kmeans_seed(FAKE, 2, 100, 128, 1, 5, 1, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert lib.kmeans_seed(FAKE, 2, 100, 128, 1, 5, 1, ctypes.c_void_p((1 << 20) + 4), FAKE, FAKE, None, FAKE,
+                           1 << 30, None) == 1                                 # u not 8-byte aligned
+    assert lib.kmeans_seed(FAKE, 2, 4, 128, 1, 5, 1, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1   # K > N
 
 
 def _table(lib, path):

@@ -416,3 +416,59 @@ def test_gauss_sum_matches_oracle(km, dtype, d, n, k, sigma2, batch):
         assert abs(tot[b] - Go.sum()) <= lim.sum(), f"gauss {dtype} D={d}: total {tot[b]} vs {Go.sum()}"
         worst = max(worst, float(np.max(err / np.maximum(S, 1e-300))))
     H.log(f"gauss {dtype} D={d} n={n} k={k} s2={sigma2} B={batch}: max error / S = {worst:.1e}")
+
+
+def _check_kpp(Xd, u, idx, eps, tag):
+    """Teacher-forced validity of k-means++ picks: with D2 from the GPU's own
+    earlier picks (oracle distances), pick j must sit in the inverse-CDF cell
+    of u_j * sum(D2) up to the relative rounding eps of the GPU's fp32 D2."""
+    n = Xd.shape[0]
+    assert idx[0] == min(int(np.floor(u[0] * n)), n - 1), tag
+    d2 = H.rowwise_sq_dist(Xd, np.broadcast_to(Xd[idx[0]], Xd.shape))
+    for j in range(1, len(u)):
+        cum = np.cumsum(d2)
+        T = cum[-1]
+        g = int(idx[j])
+        if T > 0:
+            t = u[j] * T
+            lo = cum[g - 1] if g > 0 else 0.0
+            assert d2[g] > 0 and cum[g] > t - eps * T and lo <= t + eps * T, (tag, j, g, lo, cum[g], t)
+        else:
+            assert g == min(int(np.floor(u[j] * n)), n - 1), (tag, j)
+        d2 = np.minimum(d2, H.rowwise_sq_dist(Xd, np.broadcast_to(Xd[g], Xd.shape)))
+    return d2
+
+
+@pytest.mark.parametrize("dtype,d,n,k,batch", [("bf16", 128, 20_011, 64, 1), ("fp16", 64, 9_001, 33, 3),
+                                               ("fp32", 32, 30_000, 20, 1), ("bf16", 256, 5_003, 17, 2),
+                                               ("fp16", 16, 12_345, 48, 1)])
+def test_seeding_matches_oracle(km, dtype, d, n, k, batch):
+    X, _, _, _ = _mixture(n, d, k, dtype, seed=7 * d + k, batch=batch)
+    u = torch.rand(batch, k, dtype=torch.float64, generator=torch.Generator().manual_seed(n))
+    Xg, ug = X.cuda(), u.cuda()
+    ridx, rC, _ = km.seed(Xg, ug, method="random")
+    kidx, kC, kd2 = km.seed(Xg, ug, method="kmeans++", want_d2=True)
+    torch.cuda.synchronize()
+    exact = 0
+    for b in range(batch):
+        Xd = H.decode(X[b], dtype)
+        ub = u[b].numpy()
+        assert np.array_equal(ridx[b].cpu().numpy(), oracle.seed_random(n, ub)), "random seeding rows"
+        assert np.array_equal(rC[b].cpu().numpy().astype(np.float64), Xd[ridx[b].cpu().numpy()])
+        ki = kidx[b].cpu().numpy()
+        assert np.array_equal(kC[b].cpu().numpy().astype(np.float64), Xd[ki]), "centroids are the picked rows"
+        d2 = _check_kpp(Xd, ub, ki, 3e-5, f"kmeans++ {dtype} D={d} b={b}")
+        got = kd2[b].cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - d2) <= 1e-5 * d2 + 1e-30), "final D2"
+        exact += int(np.count_nonzero(ki == oracle.kmeanspp(Xd, ub)[0]))
+    H.log(f"seeding {dtype} D={d} n={n} k={k} B={batch}: {exact} of {batch * k} k-means++ picks equal the "
+          f"free-running oracle's")
+
+
+def test_seeding_identical_rows_falls_back_to_uniform(km):
+    X = torch.full((1, 3000, 32), 0.5, dtype=torch.float16)
+    u = torch.rand(1, 9, dtype=torch.float64, generator=torch.Generator().manual_seed(2))
+    idx, C, d2 = km.seed(X.cuda(), u.cuda(), method="kmeans++", want_d2=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy()[0], oracle.seed_random(3000, u[0].numpy()))
+    assert float(d2.abs().max()) == 0.0 and torch.all(C.cpu() == 0.5)
