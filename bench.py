@@ -46,6 +46,9 @@ def parse():
                     help="also time the assignment kernel with this epilogue (top-2 labels, the Gaussian-mixture "
                          "log density with sigma2=1, or signed Gauss sums over the centroids with sigma2=1) on the "
                          "same workload")
+    ap.add_argument("--seeding", action="store_true",
+                    help="also time k-means++ seeding of the workload's K centroids (kmeans_seed) and report the "
+                         "bandwidth of its per-pick D^2 pass")
     ap.add_argument("--tune", action="store_true",
                     help="time every compiled assign configuration on this shape first (kmeans_tune) and report it")
     ap.add_argument("--probe", action="store_true",
@@ -264,6 +267,19 @@ def main():
     }
     if tuning is not None:
         out["tuning"] = tuning
+    if args.seeding:
+        su = torch.rand(C0.shape[:-1], dtype=torch.float64, generator=torch.Generator().manual_seed(3)).to(dev)
+        km.seed(X, su, method="kmeans++", ws=ws)          # warm-up (kernel loads)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        km.seed(X, su, method="kmeans++", ws=ws)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        s_ms = t_start.elapsed_time(t_end)
+        per_pick = s_ms / max(1, K - 1)
+        pass_bytes = B * N * (D * sz + 8)                 # one D^2 pass: X once, D^2 read and written
+        out["seeding"] = {"method": "kmeans++", "ms": s_ms, "ms_per_pick": per_pick,
+                          "d2_pass_bytes": pass_bytes, "gbs_per_pick": pass_bytes / (per_pick * 1e-3) / 1e9}
     if args.epilogue != "argmax":
         if args.epilogue == "top2":
             def epi():
