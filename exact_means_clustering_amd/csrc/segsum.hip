@@ -85,7 +85,7 @@ constexpr int kBuf = 8;                    // finished pieces buffered per wave
 
 // ACC selects accumulate mode (o.S_acc / o.n_acc) at compile time, so the
 // means-mode instance carries no read-modify-write code in its loop.
-template <class T, int D, bool ACC>
+template <class T, int D, bool ACC, int U>
 __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* __restrict__ X,
                                                          const uint2* __restrict__ kv, int64_t n, uint32_t nseg,
                                                          int32_t* __restrict__ off, SegOut o,
@@ -93,7 +93,6 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
   constexpr int VEC = Vec<T>::N;           // elements per 16-byte word
   constexpr int LPR = D * T::SZ / 16;      // lanes per row
   constexpr int SL = 64 / LPR;             // rows per step (lane slots)
-  constexpr int U = kSegRows;
   constexpr int NS = U / SL;               // steps per full chunk
   constexpr int NSP = NS + kRing;          // staged steps per slot (with the ring's run-ahead)
   static_assert(LPR >= 1 && LPR <= 64 && U % SL == 0, "row size");
@@ -297,11 +296,11 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
 // that cross a chunk edge, and those are dealt round-robin to the 4 waves.
 template <int D>
 __global__ __launch_bounds__(256) void seg_level2_kernel(const uint2* __restrict__ kv,
-                                                         const int32_t* __restrict__ off, int64_t n, SegOut o,
-                                                         const float* __restrict__ frag, double* __restrict__ gfrag) {
+                                                         const int32_t* __restrict__ off, int64_t n, int64_t U,
+                                                         SegOut o, const float* __restrict__ frag,
+                                                         double* __restrict__ gfrag) {
   constexpr int PER = (D + 63) / 64;
-  constexpr int64_t U = kSegRows;
-  constexpr int64_t UG = (int64_t)kSegRows * kSegGroup;
+  const int64_t UG = U * kSegGroup;
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
   const int64_t g = blockIdx.x;
@@ -367,10 +366,10 @@ constexpr int kL3Waves = 16;
 template <int D>
 __global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint2* __restrict__ kv,
                                                                    const int32_t* __restrict__ off, int64_t n,
-                                                                   int64_t ngroups, SegOut o,
+                                                                   int64_t U, int64_t ngroups, SegOut o,
                                                                    const double* __restrict__ gfrag) {
   constexpr int PER = (D + 63) / 64;
-  constexpr int64_t UG = (int64_t)kSegRows * kSegGroup;
+  const int64_t UG = U * kSegGroup;
   __shared__ double part[kL3Waves][PER * 64];
   __shared__ int64_t own_k[kL3Waves], own_s[kL3Waves], own_e[kL3Waves];
   const int lane = lane_id();
@@ -478,26 +477,36 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_
   if (i < tail_bytes) tail[i] = 0;
 }
 
+template <class T, int D, int U>
+void seg_level1_launch(const void* X, const uint2* kv, int32_t* off, int64_t n, uint32_t nseg, const SegOut& o,
+                       SegBuffers& buf, hipStream_t s) {
+  const dim3 g1((unsigned)((seg_chunks(n) + 3) / 4));
+  if (o.S_acc)
+    seg_level1_kernel<T, D, true, U><<<g1, dim3(256), 0, s>>>(reinterpret_cast<const typename T::raw*>(X), kv, n,
+                                                              nseg, off, o, buf.frag);
+  else
+    seg_level1_kernel<T, D, false, U><<<g1, dim3(256), 0, s>>>(reinterpret_cast<const typename T::raw*>(X), kv, n,
+                                                               nseg, off, o, buf.frag);
+}
+
 template <class T, int D>
 hipError_t seg_reduce_t(const void* X, const uint2* kv, int32_t* off, int64_t n, uint32_t nseg, const SegOut& o,
                         SegBuffers& buf, hipStream_t s) {
   const int64_t nchunks = seg_chunks(n);
   const int64_t ngroups = seg_groups(n);
-  const dim3 g1((unsigned)((nchunks + 3) / 4));
-  if (o.S_acc)
-    seg_level1_kernel<T, D, true><<<g1, dim3(256), 0, s>>>(reinterpret_cast<const typename T::raw*>(X), kv, n, nseg,
-                                                          off, o, buf.frag);
+  const int64_t U = seg_rows(n);
+  if (U == kSegRowsSmall)
+    seg_level1_launch<T, D, kSegRowsSmall>(X, kv, off, n, nseg, o, buf, s);
   else
-    seg_level1_kernel<T, D, false><<<g1, dim3(256), 0, s>>>(reinterpret_cast<const typename T::raw*>(X), kv, n, nseg,
-                                                           off, o, buf.frag);
+    seg_level1_launch<T, D, kSegRows>(X, kv, off, n, nseg, o, buf, s);
   if (!o.S_acc)
     empty_fill_kernel<<<dim3((unsigned)(((int64_t)nseg + 255) / 256)), dim3(256), 0, s>>>(off, nseg, D, o.C_prev,
                                                                                          o.C_new, o.counts);
   if (nchunks > 1) {
-    seg_level2_kernel<D><<<dim3((unsigned)ngroups), dim3(256), 0, s>>>(kv, off, n, o, buf.frag, buf.gfrag);
+    seg_level2_kernel<D><<<dim3((unsigned)ngroups), dim3(256), 0, s>>>(kv, off, n, U, o, buf.frag, buf.gfrag);
     if (ngroups > 1)
       seg_level3_kernel<D><<<dim3((unsigned)((ngroups + kL3Waves - 1) / kL3Waves)), dim3(kL3Waves * 64), 0, s>>>(
-          kv, off, n, ngroups, o, buf.gfrag);
+          kv, off, n, U, ngroups, o, buf.gfrag);
   }
   return hipGetLastError();
 }

@@ -24,7 +24,6 @@ namespace fkm {
 namespace {
 
 constexpr int kT = 256;
-constexpr int kIPT = kSortTile / kT;  // keys per thread per tile (16)
 
 // Source of the (key, row) pair at position i of a pass's input.  The first
 // pass makes it from the labels (row = i); later passes read the previous
@@ -63,7 +62,7 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
   return m;
 }
 
-template <class Src>
+template <class Src, int TILE>
 __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int shift, uint32_t* __restrict__ hist,
                                                         int64_t nblk) {
   __shared__ uint32_t cnt[256];
@@ -71,7 +70,8 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
   cnt[t] = 0;
   __syncthreads();
   const int64_t tile = xcd_tile(blockIdx.x, nblk);
-  const int64_t base = tile * kSortTile;
+  constexpr int kIPT = TILE / kT;  // keys per thread
+  const int64_t base = tile * TILE;
   uint32_t d[kIPT];
 #pragma unroll
   for (int r = 0; r < kIPT; ++r) {
@@ -125,14 +125,14 @@ __global__ __launch_bounds__(kT) void radix_scan_kernel(uint32_t* __restrict__ h
 // the per-wave counts become per-wave offsets, every key lands in an LDS copy
 // of the tile sorted by digit, and the tile is written out digit run by digit
 // run, so consecutive threads write consecutive addresses.
-template <class Src>
+template <class Src, int TILE>
 __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, int shift,
                                                            const uint32_t* __restrict__ hist,
                                                            const uint32_t* __restrict__ dtot, int64_t nblk,
                                                            uint2* __restrict__ out) {
-  constexpr int KW = kSortTile / 4;   // keys per wave
+  constexpr int KW = TILE / 4;        // keys per wave
   constexpr int RW = KW / 64;         // rounds per wave
-  __shared__ uint2 lkv[kSortTile];
+  __shared__ uint2 lkv[TILE];
   __shared__ uint32_t gbase[256];     // global position of LDS slot 0 of digit d's run, minus lstart[d]
   __shared__ uint32_t lstart[256];    // first LDS slot of digit d
   __shared__ uint32_t wcnt[4][256];   // per-wave digit counts, then per-wave offsets
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
 
   // the tile's elements are loaded first, so their latency overlaps the
   // histogram loads and scans below
-  const int64_t base = blk * kSortTile + (int64_t)w * KW;
+  const int64_t base = blk * TILE + (int64_t)w * KW;
   uint2 e[RW];
   uint32_t rr[RW];
 #pragma unroll
@@ -195,21 +195,28 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
     }
   }
   __syncthreads();
-  const int64_t rem = n - blk * kSortTile;
-  const int cnt = rem < kSortTile ? (int)rem : kSortTile;
+  const int64_t rem = n - blk * TILE;
+  const int cnt = rem < TILE ? (int)rem : TILE;
   for (int i = t; i < cnt; i += kT) {
     const uint2 v = lkv[i];
     out[gbase[(v.x >> shift) & 255u] + (uint32_t)i] = v;
   }
 }
 
+template <class Src, int TILE>
+hipError_t one_pass_t(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out, hipStream_t s) {
+  const int64_t nblk = (n + TILE - 1) / TILE;
+  radix_hist_kernel<Src, TILE><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist, nblk);
+  radix_scan_kernel<<<dim3(256), dim3(kT), 0, s>>>(buf.hist, nblk, buf.dtot);
+  radix_scatter_kernel<Src, TILE><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist, buf.dtot, nblk,
+                                                                            out);
+  return hipGetLastError();
+}
+
 template <class Src>
 hipError_t one_pass(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out, hipStream_t s) {
-  const int64_t nblk = sort_blocks(n);
-  radix_hist_kernel<Src><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist, nblk);
-  radix_scan_kernel<<<dim3(256), dim3(kT), 0, s>>>(buf.hist, nblk, buf.dtot);
-  radix_scatter_kernel<Src><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist, buf.dtot, nblk, out);
-  return hipGetLastError();
+  return sort_tile(n) == kSortTileSmall ? one_pass_t<Src, kSortTileSmall>(src, n, shift, buf, out, s)
+                                        : one_pass_t<Src, kSortTile>(src, n, shift, buf, out, s);
 }
 
 }  // namespace
