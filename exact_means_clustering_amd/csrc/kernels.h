@@ -87,7 +87,7 @@ hipError_t launch_inertia_reduce(const double* part, int nwg, int B, double* ine
 // ---- inverse mapping (stable LSD radix argsort) -------------------------------
 constexpr int kSortTile = 4096;       // keys per sort workgroup
 constexpr int kSortTileSmall = 1024;  // for small problems, so the sort grid still fills the chip
-inline int sort_tile(int64_t n) { return n <= ((int64_t)1 << 19) ? kSortTileSmall : kSortTile; }
+inline int sort_tile(int64_t n) { return n <= ((int64_t)1 << 21) ? kSortTileSmall : kSortTile; }
 inline int64_t sort_blocks(int64_t n) { return (n + sort_tile(n) - 1) / sort_tile(n); }
 
 // Sort elements are (key, row) pairs packed in one 8-byte word, so a pass
@@ -111,7 +111,7 @@ constexpr int kSegRows = FKM_SEG_ROWS;
 constexpr int kSegRowsSmall = 128;  // chunk rows for small problems, so the level-1 grid still fills the chip
 constexpr int kSegGroup = 8;        // level-1 chunks per level-2 group
 // Rows per level-1 chunk for n sorted rows.
-inline int seg_rows(int64_t n) { return n <= ((int64_t)1 << 19) ? kSegRowsSmall : kSegRows; }
+inline int seg_rows(int64_t n) { return n <= ((int64_t)1 << 21) ? kSegRowsSmall : kSegRows; }
 inline int64_t seg_chunks(int64_t n) { return (n + seg_rows(n) - 1) / seg_rows(n); }
 inline int64_t seg_groups(int64_t n) { return (seg_chunks(n) + kSegGroup - 1) / kSegGroup; }
 
