@@ -472,3 +472,22 @@ def test_seeding_identical_rows_falls_back_to_uniform(km):
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy()[0], oracle.seed_random(3000, u[0].numpy()))
     assert float(d2.abs().max()) == 0.0 and torch.all(C.cpu() == 0.5)
+
+
+@pytest.mark.parametrize("case", ["zipf", "one_cluster"])
+def test_update_large_problem_path(km, case):
+    """Above 2^21 rows the update uses its large chunk and tile sizes: a ragged
+    problem there, with skewed labels, against the oracle."""
+    n, k, d = 2_100_003, 5_000, 32
+    X, _, _, _ = datagen.mixture(n, d, 16, dtype="fp32", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                 weights=None, workload_code=60, seed=1)
+    if case == "zipf":
+        lab = datagen.zipf_labels(n, k, 1.1, seed=2)
+    else:
+        lab = np.full((1, n), 2_718, dtype=np.int32)
+    C_prev = torch.randn(1, k, d, generator=torch.Generator().manual_seed(3))
+    C_new, counts = km.update(X.cuda(), torch.from_numpy(lab).cuda(), C_prev.cuda())
+    torch.cuda.synchronize()
+    err = H.check_update(H.decode(X[0], "fp32"), lab[0], C_prev[0].numpy(), C_new.cpu()[0].numpy(),
+                         counts.cpu()[0].numpy(), k, tag=f"large-{case}")
+    H.log(f"update large path {case}: centroid err {err:.2e}")
