@@ -92,14 +92,35 @@ struct FitArgs {
   bool operator==(const FitArgs& o) const { return tie() == o.tie(); }
 };
 
-// iters x (prep, assign, inertia, argsort, segment reductions) on stream s
+// iters x (assign, argsort, segment reductions) on stream s.  Two
+// stand-alone launches of kmeans_assign / kmeans_update are folded into
+// neighbours: the inertia reduction runs as extra blocks of the first sort
+// histogram, and the centroid preparation for iteration t+1 is done by the
+// update of iteration t as it finishes each cluster (a kernel prepares C0).
 int enqueue_fit(const FitArgs& a, Work& w, hipStream_t s) {
+  const int64_t n = a.N * a.B;
+  const uint32_t nseg = (uint32_t)((int64_t)a.B * a.K);
+  const AssignConfig cfg = assign_pick(a.dt, a.D, a.N, a.B, a.K);
+  const int64_t nwg = (a.N + cfg.rows() - 1) / cfg.rows();
+  KM_HIP(launch_prep(a.dt, a.D, a.C0, w.chat, w.hb, a.B, a.K, s), "centroid prep launch");
   for (int t = 0; t < a.iters; ++t) {
     const float* Cs = t == 0 ? a.C0 : a.C_out;
-    if (int rc = run_assign(a.X, a.dt, a.N, a.D, a.B, Cs, a.K, a.labels, nullptr, a.inertia,
-                            a.hist ? a.hist + (int64_t)t * a.B : nullptr, w, s))
-      return rc;
-    if (int rc = run_update(a.X, a.dt, a.N, a.D, a.B, a.labels, a.K, Cs, a.C_out, nullptr, w, s)) return rc;
+    KM_HIP(launch_assign(a.dt, a.D, cfg, a.X, w.chat, w.hb, a.N, a.K, a.B, a.labels, nullptr, w.part, s),
+           "assign launch");
+    InertiaJob side;
+    side.part = w.part;
+    side.nwg = (int)nwg;
+    side.B = a.B;
+    side.inertia = a.inertia;
+    side.hist = a.hist ? a.hist + (int64_t)t * a.B : nullptr;
+    const uint2* sorted = nullptr;
+    KM_HIP(launch_argsort_labels(a.labels, a.N, a.B, a.K, w.sort, &sorted, s, &side), "argsort launch");
+    SegOut o{Cs, a.C_out, w.cnt, nullptr, nullptr};
+    o.chat = w.chat;
+    o.hb = w.hb;
+    o.K = (uint32_t)a.K;
+    o.Kp = (uint32_t)kpad(a.K);
+    KM_HIP(launch_segment_reduce(a.dt, a.D, a.X, sorted, w.off, n, nseg, o, w.seg, s), "segment reduce launch");
   }
   return KM_OK;
 }

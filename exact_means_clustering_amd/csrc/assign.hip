@@ -53,19 +53,14 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, 
     return;
   }
   const int64_t row = b * K + k;
-  constexpr int PER = (D + kWave - 1) / kWave;
-  float ss = 0.f;
+  constexpr int PER = (D + 63) / 64;
+  float c[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int d = lane + kWave * j;
-    if (d < D) {
-      const typename T::raw r = T::from_f32(C[row * D + d]);
-      Ch[row * D + d] = r;
-      const float v = T::to_f32(r);
-      ss += v * v;
-    }
+    const int d = lane + 64 * j;
+    c[j] = d < D ? C[row * D + d] : 0.f;
   }
-  ss = wave_sum_f32(ss);
+  const float ss = prep_row<T, D>(c, Ch + row * D, lane);
   // mixture log-weights enter the score as sigma2 * log w_k (soft assignment)
   if (lane == 0) hb[slot] = -0.5f * ss + (log_w ? sigma2 * log_w[row] : 0.f);
 }
@@ -532,27 +527,11 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
   }
 }
 
-// inertia[b] = fixed-order sum of part[b, :] (1024 threads, strided, then a
-// fixed tree)
-__global__ __launch_bounds__(1024) void inertia_reduce_kernel(const double* __restrict__ part, int nwg,
-                                                              double* __restrict__ inertia,
-                                                              double* __restrict__ hist, int accumulate) {
-  __shared__ double ws[16];
-  const int b = blockIdx.x;
-  double v = 0.0;
-#pragma unroll 8
-  for (int i = threadIdx.x; i < nwg; i += 1024) v += part[(int64_t)b * nwg + i];
-  v = wave_sum_f64(v);
-  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double tot = 0.0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) tot += ws[i];
-    if (accumulate) tot += inertia[b];
-    inertia[b] = tot;
-    if (hist) hist[b] = tot;
-  }
+// inertia[b] = fixed-order sum of part[b, :], one workgroup per instance
+__global__ __launch_bounds__(256) void inertia_reduce_kernel(const double* __restrict__ part, int nwg,
+                                                             double* __restrict__ inertia,
+                                                             double* __restrict__ hist, int accumulate) {
+  inertia_reduce_block(part, nwg, blockIdx.x, inertia, hist, accumulate != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -804,7 +783,7 @@ hipError_t assign_prime(int dt, int D, AssignConfig cfg) { return dispatch_dt_d<
 
 hipError_t launch_inertia_reduce(const double* part, int nwg, int B, double* inertia, double* hist, bool accumulate,
                                  hipStream_t s) {
-  inertia_reduce_kernel<<<dim3((unsigned)B), dim3(1024), 0, s>>>(part, nwg, inertia, hist, accumulate ? 1 : 0);
+  inertia_reduce_kernel<<<dim3((unsigned)B), dim3(256), 0, s>>>(part, nwg, inertia, hist, accumulate ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -181,6 +181,50 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
+// inertia[b] (+= when accumulating) = fixed-order sum of part[b, 0..nwg) by
+// one 256-thread workgroup: thread t sums part[b, t + 256 i] in order of i,
+// each wave adds its lanes, then thread 0 adds the four wave sums in order.
+__device__ __forceinline__ void inertia_reduce_block(const double* __restrict__ part, int nwg, int64_t b,
+                                                     double* __restrict__ inertia, double* __restrict__ hist,
+                                                     bool accumulate) {
+  __shared__ double ws[4];
+  double v = 0.0;
+#pragma unroll 8
+  for (int i = threadIdx.x; i < nwg; i += 256) v += part[b * nwg + i];
+  v = wave_sum_f64(v);
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+    if (accumulate) tot += inertia[b];
+    inertia[b] = tot;
+    if (hist) hist[b] = tot;
+  }
+}
+
+// Centroid preparation of one row by one wave: lane l holds the fp32
+// centroid values c[j] of dims l + 64 j.  Writes the row rounded to the
+// input type and returns sum_d RNE(c_d)^2, summed per lane in dim order and
+// then across the wave (lane 0's value is the one used).  Both the
+// preparation kernel and the update's fused preparation call this, so their
+// results are identical.
+template <class T, int D>
+__device__ __forceinline__ float prep_row(const float (&c)[(D + 63) / 64], typename T::raw* __restrict__ chat_row,
+                                          int lane) {
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < (D + 63) / 64; ++j) {
+    const int d = lane + 64 * j;
+    if (d < D) {
+      const typename T::raw r = T::from_f32(c[j]);
+      chat_row[d] = r;
+      const float v = T::to_f32(r);
+      ss = fmaf(v, v, ss);
+    }
+  }
+  return wave_sum_f32(ss);
+}
+
 // 16-byte load marked non-temporal (data read once: streamed past the caches
 // instead of displacing reusable lines).
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {

@@ -83,6 +83,15 @@ hipError_t assign_prime(int dt, int D, AssignConfig cfg);
 // value when `accumulate`); also copied to hist[b] if non-null.
 hipError_t launch_inertia_reduce(const double* part, int nwg, int B, double* inertia, double* hist,
                                  bool accumulate, hipStream_t s);
+// The same reduction as extra blocks of another launch (inertia_reduce_block
+// in common.h: one 256-thread workgroup per instance).
+struct InertiaJob {
+  const double* part = nullptr;  // [B, nwg] workgroup partials (null: no job)
+  int nwg = 0;
+  int B = 0;
+  double* inertia = nullptr;     // [B]
+  double* hist = nullptr;        // [B] copy, nullable
+};
 
 // ---- inverse mapping (stable LSD radix argsort) -------------------------------
 constexpr int kSortTile = 4096;       // keys per sort workgroup
@@ -99,8 +108,10 @@ struct SortBuffers {
 };
 // Sorts rows by key = b*K + clamp(labels[b*N+i], 0, K-1) (stable).  On return
 // *sorted points at the buffer holding the sorted (key, row) pairs.
+// `side` (nullable) is an inertia reduction that runs as extra blocks of the
+// first pass's histogram launch.
 hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K, SortBuffers& buf,
-                                 const uint2** sorted, hipStream_t s);
+                                 const uint2** sorted, hipStream_t s, const InertiaJob* side = nullptr);
 
 // ---- segment-local reductions ----------------------------------------------
 #ifndef FKM_SEG_ROWS
@@ -131,6 +142,14 @@ struct SegOut {
   int32_t* counts;
   double* S_acc;
   int64_t* n_acc;
+  // Means mode, optional: the assignment's centroid preparation fused into
+  // the update.  Every cluster with rows also gets chat[k] = RNE(C_new[k])
+  // in the input type and hb[b * Kp + l] = -0.5 ||chat[k]||^2 for key
+  // k = b * K + l, exactly as launch_prep computes them; an empty cluster
+  // keeps C_prev, so its entries (already prepared from C_prev) stay.
+  void* chat = nullptr;
+  float* hb = nullptr;
+  uint32_t K = 0, Kp = 0;
 };
 // Also writes the segment offsets off[k] = #{rows with key < k}, k in [0, nseg].
 hipError_t launch_segment_reduce(int dt, int D, const void* X, const uint2* sorted, int32_t* off, int64_t n,

@@ -35,10 +35,23 @@ __device__ __forceinline__ int frag_slot(int64_t u, int64_t U, int64_t s) {
   return (u == s / U && s != u * U) ? 1 : 0;
 }
 
-// Finish a segment: means mode writes C_new / counts, accumulate mode adds
-// into S_acc / n_acc.  `v` holds the segment sum for dims lane + 64*j.
-template <int PER>
-__device__ __forceinline__ void finish(const SegOut& o, int64_t k, int D, int lane, const double* v, int64_t cnt) {
+// The fused centroid preparation of cluster k (means mode with o.chat):
+// c[j] holds its new centroid at dims lane + 64 j.
+template <class T, int D>
+__device__ __forceinline__ void fused_prep(const SegOut& o, int64_t k, int lane, const float (&c)[(D + 63) / 64]) {
+  const float ss = prep_row<T, D>(c, reinterpret_cast<typename T::raw*>(o.chat) + k * D, lane);
+  if (lane == 0) {
+    const int64_t b = k / o.K;
+    o.hb[b * o.Kp + (k - b * o.K)] = -0.5f * ss;
+  }
+}
+
+// Finish a segment: means mode writes C_new / counts (and the fused
+// preparation), accumulate mode adds into S_acc / n_acc.  `v` holds the
+// segment sum for dims lane + 64*j.
+template <class T, int D>
+__device__ __forceinline__ void finish(const SegOut& o, int64_t k, int lane, const double* v, int64_t cnt) {
+  constexpr int PER = (D + 63) / 64;
   if (o.S_acc) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -47,12 +60,15 @@ __device__ __forceinline__ void finish(const SegOut& o, int64_t k, int D, int la
     }
     if (lane == 0) o.n_acc[k] += cnt;
   } else {
+    float c[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int d = lane + 64 * j;
-      if (d < D) o.C_new[k * D + d] = (float)(v[j] / (double)cnt);
+      c[j] = d < D ? (float)(v[j] / (double)cnt) : 0.f;
+      if (d < D) o.C_new[k * D + d] = c[j];
     }
     if (lane == 0) o.counts[k] = (int32_t)cnt;
+    if (o.chat) fused_prep<T, D>(o, k, lane, c);
   }
 }
 
@@ -175,6 +191,19 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
         if constexpr (ACC) o.n_acc[k] += nk;
         else o.counts[k] = nk;
       }
+      if constexpr (!ACC) {
+        if (kind == 0 && o.chat) {
+          // the same fp32 quotients as the stores above, at dims lane + 64 j
+          const float fc = (float)nk;
+          float cv[(D + 63) / 64];
+#pragma unroll
+          for (int j = 0; j < (D + 63) / 64; ++j) {
+            const int d = lane + 64 * j;
+            cv[j] = d < D ? bsum[w][b][d] / fc : 0.f;
+          }
+          fused_prep<T, D>(o, k, lane, cv);
+        }
+      }
     }
     nb = 0;
   };
@@ -291,19 +320,43 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
 // ---------------------------------------------------------------------------
 // level 2: per group of chunks, combine chunk fragments (fp64)
 // ---------------------------------------------------------------------------
+// Means mode: a cluster no row carries (off[k] == off[k+1]) gets count 0 and
+// keeps its previous centroid (its fused preparation, made from the previous
+// centroid, stays as it is).  One thread per cluster, 256 per block.
+__device__ __forceinline__ void empty_fill_block(int64_t blk, const int32_t* __restrict__ off, int64_t nseg, int D,
+                                                 const float* __restrict__ C_prev, float* __restrict__ C_new,
+                                                 int32_t* __restrict__ counts) {
+  const int64_t k = blk * 256 + threadIdx.x;
+  if (k >= nseg || off[k] != off[k + 1]) return;
+  counts[k] = 0;
+  if (C_new != C_prev) {  // D is a multiple of 4: copy the row as float4
+    const float4* src = reinterpret_cast<const float4*>(C_prev + k * D);
+    float4* dst = reinterpret_cast<float4*>(C_new + k * D);
+#pragma unroll 8
+    for (int d = 0; d < D / 4; ++d) dst[d] = src[d];
+  }
+}
+
 // One workgroup of 4 waves per group.  The group's segments are scanned 64
 // at a time (one coalesced load of their offsets); a ballot picks the ones
 // that cross a chunk edge, and those are dealt round-robin to the 4 waves.
-template <int D>
+// In means mode the blocks past the groups run the empty-cluster fill,
+// which needs only the offsets.
+template <class T, int D>
 __global__ __launch_bounds__(256) void seg_level2_kernel(const uint2* __restrict__ kv,
                                                          const int32_t* __restrict__ off, int64_t n, int64_t U,
-                                                         SegOut o, const float* __restrict__ frag,
+                                                         int64_t ngroups, int64_t nseg, SegOut o,
+                                                         const float* __restrict__ frag,
                                                          double* __restrict__ gfrag) {
   constexpr int PER = (D + 63) / 64;
   const int64_t UG = U * kSegGroup;
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
   const int64_t g = blockIdx.x;
+  if (g >= ngroups) {
+    empty_fill_block(g - ngroups, off, nseg, D, o.C_prev, o.C_new, o.counts);
+    return;
+  }
   const int64_t gr0 = g * UG;
   if (gr0 >= n) return;
   const int64_t gr1 = gr0 + UG < n ? gr0 + UG : n;
@@ -341,7 +394,7 @@ __global__ __launch_bounds__(256) void seg_level2_kernel(const uint2* __restrict
         }
       }
       if (s >= gr0 && e <= gr1) {
-        finish<PER>(o, k, D, lane, acc, e - s);
+        finish<T, D>(o, k, lane, acc, e - s);
       } else {
         double* gp = gfrag + (g * 2 + ((k == kf) ? 0 : 1)) * D;
 #pragma unroll
@@ -363,7 +416,7 @@ __global__ __launch_bounds__(256) void seg_level2_kernel(const uint2* __restrict
 // kL3Waves groups by itself; longer segments are then summed by all waves
 // together (interleaved by wave, combined in wave order).
 constexpr int kL3Waves = 16;
-template <int D>
+template <class T, int D>
 __global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint2* __restrict__ kv,
                                                                    const int32_t* __restrict__ off, int64_t n,
                                                                    int64_t U, int64_t ngroups, SegOut o,
@@ -399,7 +452,7 @@ __global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint2* 
           if (d < D) acc[q] += gp[d];
         }
       }
-      finish<PER>(o, k, D, lane, acc, e - s);
+      finish<T, D>(o, k, lane, acc, e - s);
       k = -1;
     }
     if (lane == 0) {
@@ -438,7 +491,7 @@ __global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint2* 
         for (int i = 0; i < kL3Waves; ++i) v += part[i][d];
         acc[q] = v;
       }
-      finish<PER>(o, k, D, lane, acc, e - s);
+      finish<T, D>(o, k, lane, acc, e - s);
     }
     __syncthreads();
   }
@@ -454,20 +507,11 @@ __global__ __launch_bounds__(256) void mean_from_sums_kernel(const double* __res
   C_new[i] = cnt[k] > 0 ? (float)(S[i] / (double)cnt[k]) : C_prev[i];
 }
 
-// Means mode: a cluster no row carries (off[k] == off[k+1]) gets count 0 and
-// keeps its previous centroid.  One thread per cluster.
+// The empty-cluster fill on its own (a problem of one chunk has no level 2).
 __global__ __launch_bounds__(256) void empty_fill_kernel(const int32_t* __restrict__ off, int64_t nseg, int D,
                                                          const float* __restrict__ C_prev, float* __restrict__ C_new,
                                                          int32_t* __restrict__ counts) {
-  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (k >= nseg || off[k] != off[k + 1]) return;
-  counts[k] = 0;
-  if (C_new != C_prev) {  // D is a multiple of 4: copy the row as float4
-    const float4* src = reinterpret_cast<const float4*>(C_prev + k * D);
-    float4* dst = reinterpret_cast<float4*>(C_new + k * D);
-#pragma unroll 8
-    for (int d = 0; d < D / 4; ++d) dst[d] = src[d];
-  }
+  empty_fill_block(blockIdx.x, off, nseg, D, C_prev, C_new, counts);
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_t n16, uint8_t* __restrict__ tail,
@@ -499,14 +543,16 @@ hipError_t seg_reduce_t(const void* X, const uint2* kv, int32_t* off, int64_t n,
     seg_level1_launch<T, D, kSegRowsSmall>(X, kv, off, n, nseg, o, buf, s);
   else
     seg_level1_launch<T, D, kSegRows>(X, kv, off, n, nseg, o, buf, s);
-  if (!o.S_acc)
-    empty_fill_kernel<<<dim3((unsigned)(((int64_t)nseg + 255) / 256)), dim3(256), 0, s>>>(off, nseg, D, o.C_prev,
-                                                                                         o.C_new, o.counts);
+  const int64_t fill_blocks = o.S_acc ? 0 : ((int64_t)nseg + 255) / 256;
   if (nchunks > 1) {
-    seg_level2_kernel<D><<<dim3((unsigned)ngroups), dim3(256), 0, s>>>(kv, off, n, U, o, buf.frag, buf.gfrag);
+    // level 2, with the empty-cluster fill in the same launch
+    seg_level2_kernel<T, D><<<dim3((unsigned)(ngroups + fill_blocks)), dim3(256), 0, s>>>(
+        kv, off, n, U, ngroups, (int64_t)nseg, o, buf.frag, buf.gfrag);
     if (ngroups > 1)
-      seg_level3_kernel<D><<<dim3((unsigned)((ngroups + kL3Waves - 1) / kL3Waves)), dim3(kL3Waves * 64), 0, s>>>(
+      seg_level3_kernel<T, D><<<dim3((unsigned)((ngroups + kL3Waves - 1) / kL3Waves)), dim3(kL3Waves * 64), 0, s>>>(
           kv, off, n, U, ngroups, o, buf.gfrag);
+  } else if (fill_blocks) {
+    empty_fill_kernel<<<dim3((unsigned)fill_blocks), dim3(256), 0, s>>>(off, nseg, D, o.C_prev, o.C_new, o.counts);
   }
   return hipGetLastError();
 }

@@ -62,9 +62,17 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
   return m;
 }
 
+// Count d of tile b goes to hist[d * dstride + b * tstride] (digit-major
+// for the scan kernel, tile-major when the scatter sums the counts itself).
+// Blocks past the nblk tiles run the side job (an inertia reduction).
 template <class Src, int TILE>
 __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int shift, uint32_t* __restrict__ hist,
-                                                        int64_t nblk) {
+                                                        int64_t nblk, int64_t dstride, int64_t tstride,
+                                                        InertiaJob side) {
+  if ((int64_t)blockIdx.x >= nblk) {
+    inertia_reduce_block(side.part, side.nwg, (int64_t)blockIdx.x - nblk, side.inertia, side.hist, false);
+    return;
+  }
   __shared__ uint32_t cnt[256];
   const int t = threadIdx.x;
   cnt[t] = 0;
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
   for (int r = 0; r < kIPT; ++r)
     if (d[r] < 256u) atomicAdd(&cnt[d[r]], 1u);
   __syncthreads();
-  hist[(int64_t)t * nblk + tile] = cnt[t];
+  hist[(int64_t)t * dstride + tile * tstride] = cnt[t];
 }
 
 // One workgroup per digit: exclusive scan of hist[d][0..nblk) in place,
@@ -117,6 +125,11 @@ __global__ __launch_bounds__(kT) void radix_scan_kernel(uint32_t* __restrict__ h
   if (threadIdx.x == 0) dtot[blockIdx.x] = running;
 }
 
+// With few tiles (kScanFreeTiles or fewer) the scatter reads the raw
+// per-tile counts (tile-major, so each load is one contiguous kilobyte) and
+// forms its own prefix, so the pass needs no scan kernel.
+constexpr int64_t kScanFreeTiles = 64;
+
 // Stable scatter of one tile.  Each wave ranks a contiguous quarter of the
 // tile (64 keys per round, in row order): a key's rank among equal digits of
 // its wave = keys of that digit in the wave's earlier rounds (a per-wave LDS
@@ -125,7 +138,7 @@ __global__ __launch_bounds__(kT) void radix_scan_kernel(uint32_t* __restrict__ h
 // the per-wave counts become per-wave offsets, every key lands in an LDS copy
 // of the tile sorted by digit, and the tile is written out digit run by digit
 // run, so consecutive threads write consecutive addresses.
-template <class Src, int TILE>
+template <class Src, int TILE, bool SCANNED>
 __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, int shift,
                                                            const uint32_t* __restrict__ hist,
                                                            const uint32_t* __restrict__ dtot, int64_t nblk,
@@ -152,11 +165,31 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
     e[r] = i < n ? src(i) : make_uint2(0u, 0u);
   }
 
-  // this tile's count of digit t, from the scanned (exclusive) histogram row
-  const uint32_t h0 = hist[(int64_t)t * nblk + blk];
-  const uint32_t h1 = blk + 1 < nblk ? hist[(int64_t)t * nblk + blk + 1] : dtot[t];
+  // this tile's count of digit t: from the scanned (exclusive) histogram
+  // row, or summed here from the raw counts of the tiles
+  uint32_t h0, h1, dt_t;
+  if constexpr (SCANNED) {
+    h0 = hist[(int64_t)t * nblk + blk];
+    h1 = blk + 1 < nblk ? hist[(int64_t)t * nblk + blk + 1] : dtot[t];
+    dt_t = dtot[t];
+  } else {
+    // tile-major counts: tile j's count of digit t is hist[j * 256 + t]
+    uint32_t c[kScanFreeTiles];
+#pragma unroll
+    for (int j = 0; j < kScanFreeTiles; ++j) c[j] = j < nblk ? hist[(int64_t)j * 256 + t] : 0u;
+    uint32_t before = 0, all = 0, own = 0;
+#pragma unroll
+    for (int j = 0; j < kScanFreeTiles; ++j) {
+      before += j < blk ? c[j] : 0u;
+      own += j == blk ? c[j] : 0u;
+      all += c[j];
+    }
+    h0 = before;
+    h1 = before + own;
+    dt_t = all;
+  }
   uint32_t tot;
-  const uint32_t dpre = block_exclusive_scan_256(dtot[t], tmp, &tot);
+  const uint32_t dpre = block_exclusive_scan_256(dt_t, tmp, &tot);
   const uint32_t ls = block_exclusive_scan_256(h1 - h0, tmp, &tot);
   lstart[t] = ls;
   gbase[t] = dpre + h0 - ls;
@@ -204,32 +237,42 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
 }
 
 template <class Src, int TILE>
-hipError_t one_pass_t(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out, hipStream_t s) {
+hipError_t one_pass_t(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out, hipStream_t s,
+                      const InertiaJob& side) {
   const int64_t nblk = (n + TILE - 1) / TILE;
-  radix_hist_kernel<Src, TILE><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist, nblk);
-  radix_scan_kernel<<<dim3(256), dim3(kT), 0, s>>>(buf.hist, nblk, buf.dtot);
-  radix_scatter_kernel<Src, TILE><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist, buf.dtot, nblk,
-                                                                            out);
+  const int64_t extra = side.part ? side.B : 0;
+  const bool scan_free = nblk <= kScanFreeTiles;
+  radix_hist_kernel<Src, TILE><<<dim3((unsigned)(nblk + extra)), dim3(kT), 0, s>>>(
+      src, n, shift, buf.hist, nblk, scan_free ? 1 : nblk, scan_free ? 256 : 1, side);
+  if (scan_free) {
+    radix_scatter_kernel<Src, TILE, false><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist,
+                                                                                     buf.dtot, nblk, out);
+  } else {
+    radix_scan_kernel<<<dim3(256), dim3(kT), 0, s>>>(buf.hist, nblk, buf.dtot);
+    radix_scatter_kernel<Src, TILE, true><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist,
+                                                                                    buf.dtot, nblk, out);
+  }
   return hipGetLastError();
 }
 
 template <class Src>
-hipError_t one_pass(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out, hipStream_t s) {
-  return sort_tile(n) == kSortTileSmall ? one_pass_t<Src, kSortTileSmall>(src, n, shift, buf, out, s)
-                                        : one_pass_t<Src, kSortTile>(src, n, shift, buf, out, s);
+hipError_t one_pass(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out, hipStream_t s,
+                    const InertiaJob& side = InertiaJob{}) {
+  return sort_tile(n) == kSortTileSmall ? one_pass_t<Src, kSortTileSmall>(src, n, shift, buf, out, s, side)
+                                        : one_pass_t<Src, kSortTile>(src, n, shift, buf, out, s, side);
 }
 
 }  // namespace
 
 hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K, SortBuffers& buf,
-                                 const uint2** sorted, hipStream_t s) {
+                                 const uint2** sorted, hipStream_t s, const InertiaJob* side) {
   const int64_t n = N * (int64_t)B;
   const uint64_t nseg = (uint64_t)B * (uint64_t)K;
   int bits = 1;
   while (bits < 32 && (1ull << bits) < nseg) ++bits;
   const int passes = (bits + 7) / 8;
   LabelSrc ls{labels, N, (uint32_t)K, B, 1.0 / (double)N};
-  hipError_t e = one_pass(ls, n, 0, buf, buf.kv[0], s);
+  hipError_t e = one_pass(ls, n, 0, buf, buf.kv[0], s, side ? *side : InertiaJob{});
   if (e != hipSuccess) return e;
   int cur = 0;
   for (int p = 1; p < passes; ++p) {
