@@ -116,21 +116,23 @@ __device__ __forceinline__ float max16(const f32x16& a) {
 
 // Running top-2 update for one lane and one 32-centroid tile: the 16 scores
 // are visited in increasing centroid index, and strict comparisons keep the
-// lower index first on equal scores.
+// lower index first on equal scores.  Written with value selects only (a
+// score not above the second best changes nothing): with branches the
+// compiler selects between the state variables by address and moves them
+// to scratch memory.
 __device__ __forceinline__ void insert_top2(const f32x16& acc, float& b1, int& i1, float& b2, int& i2, int base) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const float v = acc[r];
     const int idx = base + 8 * (r >> 2) + (r & 3);
-    if (v > b1) {
-      b2 = b1;
-      i2 = i1;
-      b1 = v;
-      i1 = idx;
-    } else if (v > b2) {
-      b2 = v;
-      i2 = idx;
-    }
+    const bool gt1 = v > b1;
+    const bool gt2 = v > b2;
+    const float nb2 = gt1 ? b1 : (gt2 ? v : b2);
+    const int ni2 = gt1 ? i1 : (gt2 ? idx : i2);
+    b1 = gt1 ? v : b1;
+    i1 = gt1 ? idx : i1;
+    b2 = nb2;
+    i2 = ni2;
   }
 }
 
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
 #pragma unroll
           for (int p = 0; p < PB; ++p) {
             if constexpr (MODE == kTop2) {
-              if (tmax[j][p] > sec[p]) insert_top2(a[j][p], best[p], bidx[p], sec[p], sidx[p], base + 32 * j);
+              insert_top2(a[j][p], best[p], bidx[p], sec[p], sidx[p], base + 32 * j);
             } else {
               improve(a[j][p], tmax[j][p], best[p], bidx[p], base + 32 * j);
             }
