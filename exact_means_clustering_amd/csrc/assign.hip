@@ -431,14 +431,22 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
 
     // squared distance of point block p to centroid k, computed directly (no
     // cancellation): each lane half sums its dims, the halves then add.
+    // With a single centroid tile every centroid is still in LDS buffer 0
+    // (row k, chunks swizzled as the tile was written), so the row is read
+    // there instead of from global memory.  The workgroup barrier after the
+    // distances (the per-workgroup sum) keeps the next job's tile load from
+    // overwriting the buffer first; kTop2 has no such barrier and reads
+    // global memory.
     auto direct_d2 = [&](int p, int k) -> float {
       const uint4* cr = reinterpret_cast<const uint4*>(Cb + (int64_t)k * D) + h * HV;
+      const bool in_lds = MODE != kTop2 && ntiles == 1;
       float part_d = 0.f;
 #pragma unroll
       for (int v = 0; v < HV; ++v) {
         float xv[Vec<T>::N], cv[Vec<T>::N];
         Vec<T>::unpack(xf[p][v], xv);
-        Vec<T>::unpack(cr[v], cv);
+        const int c = h * HV + v;
+        Vec<T>::unpack(in_lds ? tile[0][k * NCH + (c ^ (k & (NCH - 1)))] : cr[v], cv);
 #pragma unroll
         for (int e = 0; e < Vec<T>::N; ++e) {
           const float df = xv[e] - cv[e];
