@@ -122,6 +122,31 @@ def test_forced_empty_clusters(km):
     assert torch.equal(C.cpu()[0, 5], C0[0, 5]) and torch.equal(C.cpu()[0, 17], C0[0, 17])
 
 
+@pytest.mark.parametrize("dtype,d,batch", [("bf16", 128, 2), ("fp32", 32, 1), ("fp16", 64, 3)])
+def test_fit_equals_stepwise_calls(km, dtype, d, batch):
+    """kmeans_fit folds the inertia reduction into the sort and the next
+    iteration's centroid preparation into the update (empty clusters keep the
+    preparation of their unchanged centroid).  Its labels, centroids and
+    inertia history must equal the same iterations run as stand-alone
+    kmeans_assign + kmeans_update calls bit for bit, with empty clusters
+    present in every instance."""
+    X, C0, _, _ = datagen.mixture(12_345, d, 20, dtype=dtype, center_dist="normal", center_scale=2.0, sigma=1.0,
+                                  weights=None, workload_code=57, seed=3, k=33, batch=batch)
+    C0 = C0.clone()
+    C0[:, 4] = 1e4            # far away: empty in every iteration of every instance
+    C0[:, 30] = -1e4
+    Xc, C = X.cuda(), C0.cuda()
+    iters = 3
+    lab_f, C_f, J_f, hist_f = km.fit(Xc, C, iters, history=True)
+    Cs = C.clone()
+    for t in range(iters):
+        lab, _, J = km.assign(Xc, Cs)
+        assert torch.equal(J, hist_f[t]), f"{dtype}: inertia of iteration {t} differs"
+        Cs, _ = km.update(Xc, lab, Cs)
+    assert torch.equal(lab, lab_f) and torch.equal(Cs, C_f) and torch.equal(J, J_f)
+    assert torch.equal(C_f[:, 4].cpu(), C0[:, 4]) and torch.equal(C_f[:, 30].cpu(), C0[:, 30])
+
+
 def test_update_all_rows_one_cluster_large_k(km):
     """Every row in cluster 0 of K=65,536: the offsets of the other 65,535 keys
     form one range filled after the last row, and every one of those clusters
