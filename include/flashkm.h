@@ -110,6 +110,9 @@ KM_API int kmeans_update(const void* X, int32_t dtype, int64_t N, int32_t D, int
  * centroids after the LAST update.  inertia [B] fp64 device (required);
  * inertia_hist [iters, B] fp64 device (nullable) receives every round's
  * inertia.  C_out may alias C0.  Resuming is fit(X, C_t, iters - t).
+ * Every round equals one kmeans_assign followed by one kmeans_update bit for
+ * bit (internally the inertia sum and the next round's centroid preparation
+ * ride along with the update's kernels).
  * The first call with a given argument list (pointers, sizes, iters, device)
  * captures the whole fit into a HIP graph; later calls with the same list
  * replay it with one graph launch (the last 8 lists are kept; the buffers'
