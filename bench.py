@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--seeding", action="store_true",
                     help="also time k-means++ seeding of the workload's K centroids (kmeans_seed) and report the "
                          "bandwidth of its per-pick D^2 pass")
+    ap.add_argument("--zipf-update", action="store_true",
+                    help="also time kmeans_update with labels drawn from finite Zipf(1.1) over the K clusters "
+                         "(the hot-cluster stress case: the top cluster holds about 1/H_K of all rows)")
     ap.add_argument("--tune", action="store_true",
                     help="time every compiled assign configuration on this shape first (kmeans_tune) and report it")
     ap.add_argument("--probe", action="store_true",
@@ -267,6 +270,23 @@ def main():
     }
     if tuning is not None:
         out["tuning"] = tuning
+    if args.zipf_update:
+        zl = torch.from_numpy(datagen.zipf_labels(N, K, 1.1, seed=3, batch=B)).to(dev)
+        zl = zl if B > 1 else zl[0]
+        counts_top = int(torch.bincount(zl.reshape(-1).to(torch.int64)).max())
+        for _ in range(max(1, args.warmup)):
+            km.update(X, zl, C0, C_new=C_next, ws=ws)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for _ in range(args.steps):
+            km.update(X, zl, C0, C_new=C_next, ws=ws)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        z_ms = t_start.elapsed_time(t_end) / args.steps
+        out["update_zipf"] = {"labels": "finite Zipf(1.1) over K", "top_cluster_rows": counts_top, "ms": z_ms,
+                              "gbs": upd_bytes / (z_ms * 1e-3) / 1e9,
+                              "frac_hbm_peak": upd_bytes / (z_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                              "time_vs_kmeans_labels": z_ms / u_ms}
     if args.seeding:
         su = torch.rand(C0.shape[:-1], dtype=torch.float64, generator=torch.Generator().manual_seed(3)).to(dev)
         km.seed(X, su, method="kmeans++", ws=ws)          # warm-up (kernel loads)

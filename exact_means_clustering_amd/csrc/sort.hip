@@ -86,10 +86,20 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
     const int64_t i = base + r * kT + t;
     d[r] = i < n ? (src(i).x >> shift) & 255u : 256u;
   }
-  // LDS atomics: the counts are exact integers, so their order is irrelevant
+  // LDS atomics: the counts are exact integers, so their order is irrelevant.
+  // When all 64 keys of a wave's round share one digit (a skewed label
+  // distribution makes whole tiles of one cluster), one lane adds 64: 64
+  // lanes hitting one counter would serialise.
+  const int lane = t & 63;
 #pragma unroll
-  for (int r = 0; r < kIPT; ++r)
-    if (d[r] < 256u) atomicAdd(&cnt[d[r]], 1u);
+  for (int r = 0; r < kIPT; ++r) {
+    const uint32_t d0 = __builtin_amdgcn_readfirstlane(d[r]);
+    if (__ballot(d[r] == d0) == ~0ull) {
+      if (lane == 0 && d0 < 256u) atomicAdd(&cnt[d0], 64u);
+    } else if (d[r] < 256u) {
+      atomicAdd(&cnt[d[r]], 1u);
+    }
+  }
   __syncthreads();
   hist[(int64_t)t * dstride + tile * tstride] = cnt[t];
 }
