@@ -110,9 +110,14 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
   constexpr int LPR = D * T::SZ / 16;      // lanes per row
   constexpr int SL = 64 / LPR;             // rows per step (lane slots)
   constexpr int NS = U / SL;               // steps per full chunk
-  constexpr int NSP = NS + kRing;          // staged steps per slot (with the ring's run-ahead)
+  // Staged steps per slot.  The loop runs whole rounds of kRing steps, and
+  // step i of a round reads the row ids of step i + kRing (four steps per
+  // 16-byte load), so the staging must cover roundup(NS, kRing) + kRing
+  // steps: entries past the chunk hold kNoKey and the chunk's last row.
+  constexpr int NSP = (NS + kRing - 1) / kRing * kRing + kRing;
   static_assert(LPR >= 1 && LPR <= 64 && U % SL == 0, "row size");
   static_assert(kRing % 4 == 0 && NS % 4 == 0, "steps are read four at a time");
+  static_assert(NSP % 4 == 0 && NSP >= NS + kRing, "the staging covers every step the ring reads");
   __shared__ __align__(16) uint32_t tkey[4][SL][NSP];
   __shared__ __align__(16) uint32_t trow[4][SL][NSP];
   __shared__ __align__(16) float bsum[4][kBuf][D];
