@@ -177,6 +177,9 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
   using Cfg = AssignCfg<T, D, PB, W>;
   constexpr int NCH = Cfg::NCH, HV = Cfg::HV, STEPS = Cfg::STEPS;
   constexpr int TK = Cfg::TK;
+  // the delayed reduction holds a second set of accumulators; the other
+  // epilogues' larger running state leaves no room for it at two point blocks
+  constexpr bool DELAY = Cfg::DELAY && (MODE == kArgmax || PB == 1);
   __shared__ uint4 tile[2][Cfg::TILE_CH];
   __shared__ __align__(16) float tb[2][TK];  // read back as float4
   __shared__ __align__(16) float tw[MODE == kGauss ? 2 : 1][MODE == kGauss ? TK : 4];  // kGauss: weights
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
     f32x16 prev[G][PB];
     f32x16 wprev[G];  // kGauss: the weights of the delayed group
     int prev_base = 0;
-    if constexpr (Cfg::DELAY) {
+    if constexpr (DELAY) {
 #pragma unroll
       for (int j = 0; j < G; ++j)
 #pragma unroll
@@ -404,7 +407,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
 #pragma unroll
             for (int p = 0; p < PB; ++p) acc[j][p] = Mfma<T>::step(af[j], xf[p], st, acc[j][p]);
         const int base = t * TK + g * G * 32 + 4 * h;
-        if constexpr (Cfg::DELAY) {
+        if constexpr (DELAY) {
           reduce_group(prev, prev_base, wprev);
 #pragma unroll
           for (int i = 0; i < STEPS * PB * G; ++i) {
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
       wait_tile();
       __syncthreads();
     }
-    if constexpr (Cfg::DELAY) reduce_group(prev, prev_base, wprev);
+    if constexpr (DELAY) reduce_group(prev, prev_base, wprev);
 
     // squared distance of point block p to centroid k, computed directly (no
     // cancellation): each lane half sums its dims, the halves then add.
@@ -608,8 +611,11 @@ constexpr bool cfg_compiled(int row_bytes, int pb, int waves) {
   return false;
 }
 
-// The top-2 and soft epilogues are compiled for one configuration per row
-// size (one point block per wave; 8 waves when the row allows it).
+// The top-2, soft and Gauss epilogues are compiled for one configuration per
+// row size: two point blocks and 8 waves where the argmax kernel has that
+// configuration (rows of at most 256 bytes), else one block and 8 waves
+// when the row allows it.
+constexpr int mode_pb(int row_bytes) { return row_bytes <= 256 ? 2 : 1; }
 constexpr int mode_waves(int row_bytes) { return row_bytes <= 512 ? 8 : 4; }
 
 template <class T, int D, int MODE>
@@ -629,9 +635,9 @@ hipError_t assign_cfg(AssignConfig c, const void* X, const void* Chat, const flo
     FKM_CASE(1, 4)
 #undef FKM_CASE
   } else {
-    constexpr int MW = mode_waves(rb);
-    if (c.pb == 1 && c.waves == MW)
-      return assign_t<T, D, 1, MW, MODE>(X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
+    constexpr int MP = mode_pb(rb), MW = mode_waves(rb);
+    if (c.pb == MP && c.waves == MW)
+      return assign_t<T, D, MP, MW, MODE>(X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
   }
   return hipErrorInvalidValue;
 }
@@ -752,7 +758,10 @@ hipError_t launch_assign(int dt, int D, AssignConfig cfg, const void* X, const v
                                 s);
 }
 
-AssignConfig mode_config(int dt, int D) { return AssignConfig{1, mode_waves(D * dtype_size(dt))}; }
+AssignConfig mode_config(int dt, int D) {
+  const int rb = D * dtype_size(dt);
+  return AssignConfig{mode_pb(rb), mode_waves(rb)};
+}
 
 hipError_t launch_assign_top2(int dt, int D, const void* X, const void* Chat, const float* hb, int64_t N, int K, int B,
                               int32_t* labels2, float* d2, hipStream_t s) {
