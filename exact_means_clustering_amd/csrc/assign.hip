@@ -177,9 +177,9 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
   using Cfg = AssignCfg<T, D, PB, W>;
   constexpr int NCH = Cfg::NCH, HV = Cfg::HV, STEPS = Cfg::STEPS;
   constexpr int TK = Cfg::TK;
-  // the delayed reduction holds a second set of accumulators; the other
-  // epilogues' larger running state leaves no room for it at two point blocks
-  constexpr bool DELAY = Cfg::DELAY && (MODE == kArgmax || PB == 1);
+  // the delayed reduction holds a second set of accumulators: there is room
+  // for it at one point block, and at two for the argmax epilogue only
+  constexpr bool DELAY = Cfg::DELAY && (MODE == kArgmax || PB == 1) && PB <= 2;
   __shared__ uint4 tile[2][Cfg::TILE_CH];
   __shared__ __align__(16) float tb[2][TK];  // read back as float4
   __shared__ __align__(16) float tw[MODE == kGauss ? 2 : 1][MODE == kGauss ? TK : 4];  // kGauss: weights
@@ -602,12 +602,14 @@ hipError_t assign_t(const void* X, const void* Chat, const float* hb, int64_t N,
 // Compiled configurations.  The point fragments of PB blocks take
 // PB * D * SZ / 8 VGPRs per lane, so deep blocking is limited to short rows.
 // (8-wave workgroups run two waves per SIMD, i.e. 256 registers per wave.)
-constexpr bool cfg_compiled(int row_bytes, int pb, int waves) {
+constexpr bool cfg_compiled(int elem_bytes, int row_bytes, int pb, int waves) {
   if (pb == 1 && waves == 4) return true;
   if (pb == 1 && waves == 8) return row_bytes <= 512;
   if (pb == 2 && waves == 4) return row_bytes <= 512;
   if (pb == 2 && waves == 8) return row_bytes <= 256;
   if (pb == 4 && waves == 4) return row_bytes <= 256;
+  // (fp32 rows of 256 bytes spill inside the tile loop at three blocks)
+  if (pb == 3 && waves == 8) return row_bytes <= (elem_bytes == 2 ? 256 : 128);
   return false;
 }
 
@@ -624,11 +626,12 @@ hipError_t assign_cfg(AssignConfig c, const void* X, const void* Chat, const flo
   constexpr int rb = D * T::SZ;
   if constexpr (MODE == kArgmax) {
 #define FKM_CASE(PB_, W_)                                                                      \
-    if constexpr (cfg_compiled(rb, PB_, W_)) {                                                 \
+    if constexpr (cfg_compiled(T::SZ, rb, PB_, W_)) {                                          \
       if (c.pb == PB_ && c.waves == W_)                                                        \
         return assign_t<T, D, PB_, W_, MODE>(X, Chat, hb, N, K, B, labels, min_d2, part, soft, s); \
     }
     FKM_CASE(4, 4)
+    FKM_CASE(3, 8)
     FKM_CASE(2, 8)
     FKM_CASE(2, 4)
     FKM_CASE(1, 8)
@@ -647,10 +650,11 @@ hipError_t assign_prime_cfg(AssignConfig c) {
   constexpr int rb = D * T::SZ;
   int slots = 0;
 #define FKM_CASE(PB_, W_)                                              \
-  if constexpr (cfg_compiled(rb, PB_, W_)) {                           \
+  if constexpr (cfg_compiled(T::SZ, rb, PB_, W_)) {                    \
     if (c.pb == PB_ && c.waves == W_) return assign_slots<T, D, PB_, W_, kArgmax>(&slots); \
   }
   FKM_CASE(4, 4)
+  FKM_CASE(3, 8)
   FKM_CASE(2, 8)
   FKM_CASE(2, 4)
   FKM_CASE(1, 8)
@@ -719,10 +723,12 @@ AssignConfig env_override() {
 }
 }  // namespace
 
-bool assign_config_compiled(int dt, int D, AssignConfig c) { return cfg_compiled(D * dtype_size(dt), c.pb, c.waves); }
+bool assign_config_compiled(int dt, int D, AssignConfig c) {
+  return cfg_compiled(dtype_size(dt), D * dtype_size(dt), c.pb, c.waves);
+}
 
 int assign_configs(int dt, int D, AssignConfig* out, int cap) {
-  const AssignConfig all[] = {{4, 4}, {2, 8}, {2, 4}, {1, 8}, {1, 4}};
+  const AssignConfig all[] = {{4, 4}, {3, 8}, {2, 8}, {2, 4}, {1, 8}, {1, 4}};
   int n = 0;
   for (const AssignConfig& c : all)
     if (n < cap && assign_config_compiled(dt, D, c)) out[n++] = c;
@@ -732,15 +738,22 @@ int assign_configs(int dt, int D, AssignConfig* out, int cap) {
 AssignConfig assign_pick(int dt, int D, int64_t N, int B, int K) {
   const int rb = D * dtype_size(dt);
   const AssignConfig o = env_override();
-  if (o.pb && cfg_compiled(rb, o.pb, o.waves)) return o;
+  const int sz = dtype_size(dt);
+  if (o.pb && cfg_compiled(sz, rb, o.pb, o.waves)) return o;
   AssignConfig tuned;
-  if (tune_lookup(dt, D, N, B, K, &tuned) && cfg_compiled(rb, tuned.pb, tuned.waves)) return tuned;
+  if (tune_lookup(dt, D, N, B, K, &tuned) && cfg_compiled(sz, rb, tuned.pb, tuned.waves)) return tuned;
   // Two waves per SIMD (8-wave workgroups) so one wave's argmax epilogue
   // overlaps the other's MFMAs; the deepest register blocking that still
-  // leaves >= 4 workgroups per CU.
+  // leaves >= 4 workgroups per CU.  Three point blocks (no delayed
+  // reduction) reuse each centroid fragment 1.5x more and pay off when every
+  // workgroup sweeps many tiles over many jobs (measured: 3.7% at N = 2^23,
+  // K = 65,536); with few tiles per job or few jobs per workgroup the job
+  // overheads and the uneven last round lose more.
+  const bool long_sweep = K >= 8192 && (N + 767) / 768 * (int64_t)B >= 4096;
+  if (long_sweep && cfg_compiled(sz, rb, 3, 8)) return AssignConfig{3, 8};
   const AssignConfig order[] = {{2, 8}, {1, 8}, {1, 4}};
   for (const AssignConfig& c : order) {
-    if (!cfg_compiled(rb, c.pb, c.waves)) continue;
+    if (!cfg_compiled(sz, rb, c.pb, c.waves)) continue;
     const int64_t wgs = (N + c.rows() - 1) / c.rows() * (int64_t)B;
     if (wgs >= 1024) return c;
   }

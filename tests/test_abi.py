@@ -153,7 +153,8 @@ def test_tuning_table_files(lib, tmp_path):
         ("2 96 500 1 10 1 4\n", b"unsupported shape"),          # D not supported
         ("2 64 5 1 10 1 4\n", b"unsupported shape"),            # N < K
         ("0 256 500 1 10 2 8\n", b"not compiled"),              # fp32 D=256 rows are 1 KB: pb=2 x 8 waves not built
-        ("2 64 500 1 10 3 8\n", b"not compiled"),
+        ("2 64 500 1 10 3 4\n", b"not compiled"),              # no (3 blocks, 4 waves) configuration
+        ("0 64 500 1 10 3 8\n", b"not compiled"),              # fp32 rows of 256 B: 3 blocks would spill
     ]
     for i, (text, msg) in enumerate(cases):
         f = tmp_path / f"bad{i}.txt"
