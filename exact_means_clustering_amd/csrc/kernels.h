@@ -98,12 +98,27 @@ constexpr int kSortTile = 4096;       // keys per sort workgroup
 constexpr int kSortTileSmall = 1024;  // for small problems, so the sort grid still fills the chip
 inline int sort_tile(int64_t n) { return n <= ((int64_t)1 << 21) ? kSortTileSmall : kSortTile; }
 inline int64_t sort_blocks(int64_t n) { return (n + sort_tile(n) - 1) / sort_tile(n); }
+// A pass whose scatter sums the per-tile counts itself, with no scan kernel,
+// covers at most this many tiles (per segment, for a segmented pass).
+constexpr int64_t kScanFreeTiles = 64;
+// B > 1 instances with K <= 256 sort in one segmented pass (each instance by
+// its label) when an instance spans at most kScanFreeTiles tiles.
+inline bool sort_segmented(int64_t N, int B, int K) {
+  return B > 1 && K <= 256 && (N + sort_tile(N * B) - 1) / sort_tile(N * B) <= kScanFreeTiles;
+}
+// Tiles the sort's histogram must hold: a segmented pass tiles each
+// instance separately, so its ragged tails can add up to B - 1 tiles.
+inline int64_t sort_hist_tiles(int64_t N, int B, int K) {
+  const int64_t plain = sort_blocks(N * B);
+  const int64_t seg = sort_segmented(N, B, K) ? (N + sort_tile(N * B) - 1) / sort_tile(N * B) * B : 0;
+  return plain > seg ? plain : seg;
+}
 
 // Sort elements are (key, row) pairs packed in one 8-byte word, so a pass
 // reads and writes each element with a single access.
 struct SortBuffers {
   uint2* kv[2];     // [n] each: ping-pong pair buffers
-  uint32_t* hist;   // [256 * nblk]
+  uint32_t* hist;   // [256 * sort_hist_tiles(N, B, K)]
   uint32_t* dtot;   // [256]
 };
 // Sorts rows by key = b*K + clamp(labels[b*N+i], 0, K-1) (stable).  On return

@@ -50,6 +50,29 @@ struct PairSrc {
   __device__ __forceinline__ uint2 operator()(int64_t i) const { return kv[i]; }
 };
 
+// Segment geometry of a segmented pass (segN elements per segment, ntb
+// tiles each, key offset kseg per segment); unused by a plain pass.
+struct Segs {
+  int64_t segN = 0, ntb = 1;
+  uint32_t kseg = 0;
+};
+// Where tile g lies: its elements are row0 + [first, min(first + TILE, lim)),
+// g0 is the segment's first tile and koff its key offset.
+struct TilePos {
+  int64_t row0, first, lim, g0, blk;
+  uint32_t koff;
+};
+template <bool SEG, int TILE>
+__device__ __forceinline__ TilePos tile_pos_t(int64_t g, int64_t n, const Segs& s) {
+  if constexpr (SEG) {
+    const int64_t sb = g / s.ntb;
+    const int64_t blk = g - sb * s.ntb;
+    return TilePos{sb * s.segN, blk * TILE, s.segN, sb * s.ntb, blk, (uint32_t)sb * s.kseg};
+  } else {
+    return TilePos{0, g * TILE, n, 0, g, 0u};
+  }
+}
+
 // Mask of the active lanes of this wave whose 8-bit digit equals mine.
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
   uint64_t m = __ballot(valid);
@@ -65,10 +88,13 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
 // Count d of tile b goes to hist[d * dstride + b * tstride] (digit-major
 // for the scan kernel, tile-major when the scatter sums the counts itself).
 // Blocks past the nblk tiles run the side job (an inertia reduction).
-template <class Src, int TILE>
+// SEG: the n elements are consecutive segments of segN, each cut into ntb
+// tiles of its own (the last one ragged), and the digit is taken from
+// key - segment * kseg, so one pass sorts every segment by its local key.
+template <class Src, int TILE, bool SEG>
 __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int shift, uint32_t* __restrict__ hist,
                                                         int64_t nblk, int64_t dstride, int64_t tstride,
-                                                        InertiaJob side) {
+                                                        Segs seg, InertiaJob side) {
   if ((int64_t)blockIdx.x >= nblk) {
     inertia_reduce_block(side.part, side.nwg, (int64_t)blockIdx.x - nblk, side.inertia, side.hist, false);
     return;
@@ -78,13 +104,13 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
   cnt[t] = 0;
   __syncthreads();
   const int64_t tile = xcd_tile(blockIdx.x, nblk);
+  const TilePos p = tile_pos_t<SEG, TILE>(tile, n, seg);
   constexpr int kIPT = TILE / kT;  // keys per thread
-  const int64_t base = tile * TILE;
   uint32_t d[kIPT];
 #pragma unroll
   for (int r = 0; r < kIPT; ++r) {
-    const int64_t i = base + r * kT + t;
-    d[r] = i < n ? (src(i).x >> shift) & 255u : 256u;
+    const int64_t li = p.first + r * kT + t;
+    d[r] = li < p.lim ? ((src(p.row0 + li).x - p.koff) >> shift) & 255u : 256u;
   }
   // LDS atomics: the counts are exact integers, so their order is irrelevant.
   // When all 64 keys of a wave's round share one digit (a skewed label
@@ -138,7 +164,6 @@ __global__ __launch_bounds__(kT) void radix_scan_kernel(uint32_t* __restrict__ h
 // With few tiles (kScanFreeTiles or fewer) the scatter reads the raw
 // per-tile counts (tile-major, so each load is one contiguous kilobyte) and
 // forms its own prefix, so the pass needs no scan kernel.
-constexpr int64_t kScanFreeTiles = 64;
 
 // Stable scatter of one tile.  Each wave ranks a contiguous quarter of the
 // tile (64 keys per round, in row order): a key's rank among equal digits of
@@ -148,11 +173,14 @@ constexpr int64_t kScanFreeTiles = 64;
 // the per-wave counts become per-wave offsets, every key lands in an LDS copy
 // of the tile sorted by digit, and the tile is written out digit run by digit
 // run, so consecutive threads write consecutive addresses.
-template <class Src, int TILE, bool SCANNED>
+// SEG (scan-free only): the tile sums the counts of its own segment's tiles
+// and writes into that segment's part of the output.
+template <class Src, int TILE, bool SCANNED, bool SEG>
 __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, int shift,
                                                            const uint32_t* __restrict__ hist,
                                                            const uint32_t* __restrict__ dtot, int64_t nblk,
-                                                           uint2* __restrict__ out) {
+                                                           Segs seg, uint2* __restrict__ out) {
+  static_assert(!(SCANNED && SEG), "a segmented pass sums its own counts");
   constexpr int KW = TILE / 4;        // keys per wave
   constexpr int RW = KW / 64;         // rounds per wave
   __shared__ uint2 lkv[TILE];
@@ -162,21 +190,24 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
   __shared__ uint32_t tmp[4];
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
-  const int64_t blk = xcd_tile(blockIdx.x, nblk);  // the tile this workgroup sorts
+  const int64_t g = xcd_tile(blockIdx.x, nblk);  // the tile this workgroup sorts
+  const TilePos p = tile_pos_t<SEG, TILE>(g, n, seg);
+  const int64_t blk = p.blk;                      // its index inside the segment
+  const int64_t tiles = SEG ? seg.ntb : nblk;     // tiles of the segment
 
   // the tile's elements are loaded first, so their latency overlaps the
   // histogram loads and scans below
-  const int64_t base = blk * TILE + (int64_t)w * KW;
+  const int64_t first = p.first + (int64_t)w * KW;
   uint2 e[RW];
   uint32_t rr[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    const int64_t i = base + r * 64 + lane;
-    e[r] = i < n ? src(i) : make_uint2(0u, 0u);
+    const int64_t li = first + r * 64 + lane;
+    e[r] = li < p.lim ? src(p.row0 + li) : make_uint2(0u, 0u);
   }
 
   // this tile's count of digit t: from the scanned (exclusive) histogram
-  // row, or summed here from the raw counts of the tiles
+  // row, or summed here from the raw counts of the segment's tiles
   uint32_t h0, h1, dt_t;
   if constexpr (SCANNED) {
     h0 = hist[(int64_t)t * nblk + blk];
@@ -186,7 +217,7 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
     // tile-major counts: tile j's count of digit t is hist[j * 256 + t]
     uint32_t c[kScanFreeTiles];
 #pragma unroll
-    for (int j = 0; j < kScanFreeTiles; ++j) c[j] = j < nblk ? hist[(int64_t)j * 256 + t] : 0u;
+    for (int j = 0; j < kScanFreeTiles; ++j) c[j] = j < tiles ? hist[(p.g0 + j) * 256 + t] : 0u;
     uint32_t before = 0, all = 0, own = 0;
 #pragma unroll
     for (int j = 0; j < kScanFreeTiles; ++j) {
@@ -202,16 +233,15 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
   const uint32_t dpre = block_exclusive_scan_256(dt_t, tmp, &tot);
   const uint32_t ls = block_exclusive_scan_256(h1 - h0, tmp, &tot);
   lstart[t] = ls;
-  gbase[t] = dpre + h0 - ls;
+  gbase[t] = (uint32_t)p.row0 + dpre + h0 - ls;
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) wcnt[ww][t] = 0;
   __syncthreads();
 
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    const int64_t i = base + r * 64 + lane;
-    const bool valid = i < n;
-    const uint32_t d = (e[r].x >> shift) & 255u;
+    const bool valid = first + r * 64 + lane < p.lim;
+    const uint32_t d = ((e[r].x - p.koff) >> shift) & 255u;
     const uint64_t m = match_digit(d, valid);
     const uint32_t lrank = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
     const uint32_t before = wcnt[w][d];
@@ -231,18 +261,17 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    const int64_t i = base + r * 64 + lane;
-    if (i < n) {
-      const uint32_t d = (e[r].x >> shift) & 255u;
+    if (first + r * 64 + lane < p.lim) {
+      const uint32_t d = ((e[r].x - p.koff) >> shift) & 255u;
       lkv[lstart[d] + wcnt[w][d] + rr[r]] = e[r];
     }
   }
   __syncthreads();
-  const int64_t rem = n - blk * TILE;
+  const int64_t rem = p.lim - p.first;
   const int cnt = rem < TILE ? (int)rem : TILE;
   for (int i = t; i < cnt; i += kT) {
     const uint2 v = lkv[i];
-    out[gbase[(v.x >> shift) & 255u] + (uint32_t)i] = v;
+    out[gbase[((v.x - p.koff) >> shift) & 255u] + (uint32_t)i] = v;
   }
 }
 
@@ -252,15 +281,15 @@ hipError_t one_pass_t(Src src, int64_t n, int shift, SortBuffers& buf, uint2* ou
   const int64_t nblk = (n + TILE - 1) / TILE;
   const int64_t extra = side.part ? side.B : 0;
   const bool scan_free = nblk <= kScanFreeTiles;
-  radix_hist_kernel<Src, TILE><<<dim3((unsigned)(nblk + extra)), dim3(kT), 0, s>>>(
-      src, n, shift, buf.hist, nblk, scan_free ? 1 : nblk, scan_free ? 256 : 1, side);
+  radix_hist_kernel<Src, TILE, false><<<dim3((unsigned)(nblk + extra)), dim3(kT), 0, s>>>(
+      src, n, shift, buf.hist, nblk, scan_free ? 1 : nblk, scan_free ? 256 : 1, Segs{}, side);
   if (scan_free) {
-    radix_scatter_kernel<Src, TILE, false><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist,
-                                                                                     buf.dtot, nblk, out);
+    radix_scatter_kernel<Src, TILE, false, false><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(
+        src, n, shift, buf.hist, buf.dtot, nblk, Segs{}, out);
   } else {
     radix_scan_kernel<<<dim3(256), dim3(kT), 0, s>>>(buf.hist, nblk, buf.dtot);
-    radix_scatter_kernel<Src, TILE, true><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(src, n, shift, buf.hist,
-                                                                                    buf.dtot, nblk, out);
+    radix_scatter_kernel<Src, TILE, true, false><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(
+        src, n, shift, buf.hist, buf.dtot, nblk, Segs{}, out);
   }
   return hipGetLastError();
 }
@@ -270,6 +299,23 @@ hipError_t one_pass(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out,
                     const InertiaJob& side = InertiaJob{}) {
   return sort_tile(n) == kSortTileSmall ? one_pass_t<Src, kSortTileSmall>(src, n, shift, buf, out, s, side)
                                         : one_pass_t<Src, kSortTile>(src, n, shift, buf, out, s, side);
+}
+
+// One segmented pass: B segments of N keys b*K + label with K <= 256, each
+// tiled on its own, ntb = ceil(N / TILE) <= kScanFreeTiles tiles per segment,
+// B * ntb tiles in all (the histogram holds sort_seg_blocks(N, B) tiles).
+template <int TILE>
+hipError_t seg_pass_t(const LabelSrc& src, int64_t N, int B, uint32_t K, SortBuffers& buf, uint2* out,
+                      hipStream_t s, const InertiaJob& side) {
+  const int64_t n = N * (int64_t)B;
+  const Segs sg{N, (N + TILE - 1) / TILE, K};
+  const int64_t nblk = sg.ntb * B;
+  const int64_t extra = side.part ? side.B : 0;
+  radix_hist_kernel<LabelSrc, TILE, true><<<dim3((unsigned)(nblk + extra)), dim3(kT), 0, s>>>(
+      src, n, 0, buf.hist, nblk, 1, 256, sg, side);
+  radix_scatter_kernel<LabelSrc, TILE, false, true><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(
+      src, n, 0, buf.hist, buf.dtot, nblk, sg, out);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -282,6 +328,14 @@ hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K,
   while (bits < 32 && (1ull << bits) < nseg) ++bits;
   const int passes = (bits + 7) / 8;
   LabelSrc ls{labels, N, (uint32_t)K, B, 1.0 / (double)N};
+  if (passes > 1 && sort_segmented(N, B, K)) {
+    // instances arrive one after another, so sorting each by its label alone
+    // gives the order of the key b*K + label in one pass
+    *sorted = buf.kv[0];
+    return sort_tile(n) == kSortTileSmall
+               ? seg_pass_t<kSortTileSmall>(ls, N, B, (uint32_t)K, buf, buf.kv[0], s, side ? *side : InertiaJob{})
+               : seg_pass_t<kSortTile>(ls, N, B, (uint32_t)K, buf, buf.kv[0], s, side ? *side : InertiaJob{});
+  }
   hipError_t e = one_pass(ls, n, 0, buf, buf.kv[0], s, side ? *side : InertiaJob{});
   if (e != hipSuccess) return e;
   int cur = 0;

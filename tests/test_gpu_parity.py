@@ -197,6 +197,36 @@ def test_batched_equals_unbatched(km):
     assert torch.equal(l2, lb[0]) and torch.equal(C2, Cb[0])
 
 
+@pytest.mark.parametrize("n,k,batch", [(3001, 256, 7), (65_536, 200, 3), (70_001, 256, 2)])
+def test_batched_update_skewed_labels(km, n, k, batch):
+    """Batched update against the oracle, instance by instance.  With K <= 256
+    the key sort takes one pass over tiles that stay inside an instance while
+    an instance spans at most 64 tiles of 1024 keys (a ragged tail in the
+    first case, exactly 64 tiles in the second), and two passes beyond that
+    (the third).  Labels: one instance entirely in the last cluster, one
+    holding only the first and last clusters, one Zipf-skewed, the rest
+    uniform."""
+    d = 64
+    X, _, _, _ = datagen.mixture(n, d, 8, dtype="fp16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                 weights=None, workload_code=57, seed=n, batch=batch)
+    rng = np.random.default_rng(k)
+    lab = rng.integers(0, k, size=(batch, n)).astype(np.int32)
+    lab[0] = k - 1
+    lab[1] = np.where(rng.random(n) < 0.5, 0, k - 1)
+    if batch > 2:
+        lab[2] = datagen.zipf_labels(n, k, 1.1, seed=3)[0]
+    C_prev = torch.randn(batch, k, d, generator=torch.Generator().manual_seed(5))
+    C_new, counts = km.update(X.cuda(), torch.from_numpy(lab).cuda(), C_prev.cuda())
+    torch.cuda.synchronize()
+    C_new, counts = C_new.cpu().numpy(), counts.cpu().numpy()
+    worst = 0.0
+    for b in range(batch):
+        err = H.check_update(H.decode(X[b], "fp16"), lab[b], C_prev[b].numpy(), C_new[b], counts[b], k,
+                             tag=f"batched n={n} k={k} b={b}")
+        worst = max(worst, err)
+    H.log(f"batched update n={n} k={k} B={batch}: worst centroid err {worst:.2e}")
+
+
 def test_determinism_and_resume(km):
     p = datagen.make("c3", n=50000, k=777, seed=6)
     X, C0 = p.X.cuda(), p.C0.cuda()
