@@ -16,6 +16,11 @@
 // order is fully determined: equal keys keep their row order.  Histogram
 // counts use LDS atomics (exact integers, so order-free).  No workgroup ever
 // waits on another.
+// With few tiles a pass drops its scan kernel: the histogram is stored
+// tile-major and each scatter workgroup sums the counts it needs.  Batched
+// keys with K <= 256 take a single segmented pass: the instances arrive one
+// after another, so tiles that stay inside one instance and sort by the label
+// alone produce the order of b*K + label.
 #include "common.h"
 #include "kernels.h"
 
