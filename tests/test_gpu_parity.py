@@ -304,8 +304,9 @@ def test_fit_graph_replays_match_direct_launches(km, case, monkeypatch):
     """kmeans_fit replays a captured HIP graph for a repeated argument list.
     Every replay, with other GPU work and host synchronisation in between, and
     with the input contents changed between calls, must equal direct launches
-    bit for bit."""
-    p = datagen.make(case, n=6000, k=40, batch=3, seed=11) if case == "c4" else datagen.make(case, n=20000, seed=11)
+    bit for bit.  The batched case has B*K = 300 keys, so its sort is the
+    one-pass segmented sort."""
+    p = datagen.make(case, n=6000, k=100, batch=3, seed=11) if case == "c4" else datagen.make(case, n=20000, seed=11)
     X = (p.X if p.B > 1 else p.X[0]).cuda()
     C0 = (p.C0 if p.B > 1 else p.C0[0]).cuda()
     B = p.B
