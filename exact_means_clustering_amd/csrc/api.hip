@@ -125,7 +125,7 @@ int enqueue_fit(const FitArgs& a, Work& w, hipStream_t s) {
   return KM_OK;
 }
 
-// A fit is a fixed sequence of about a dozen kernels per iteration whose
+// A fit is a fixed sequence of 6 to 10 kernels per iteration whose
 // arguments are only pointers and sizes, so it is captured once into a HIP
 // graph and replayed: one graph launch enqueues every kernel, which removes
 // the per-launch host overhead that dominates small problems.  Graphs are
@@ -266,8 +266,9 @@ int kmeans_gauss_sum(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t
   hipStream_t s = (hipStream_t)stream;
   KM_HIP(launch_prep(dtype, D, Y, wk.chat, wk.hb, B, K, s), "source prep launch");
   KM_HIP(launch_pad_weights(w, wk.wpad, B, K, s), "weight pad launch");
-  // labels of the nearest source go to the workspace's counts region (B*K >= B*N is not
-  // guaranteed, so they use the sort buffers, which hold 2*B*N words)
+  // the kernel also writes each point's nearest source, which this entry point
+  // does not return: it lands in the first sort buffer (B*N pairs of words),
+  // since the counts region holds only B*K entries and K may be below N
   int32_t* lab = reinterpret_cast<int32_t*>(wk.sort.kv[0]);
   const SoftArgs sa{nullptr, 1.4426950408889634f / sigma2, 0.5f / sigma2, wk.wpad};
   KM_HIP(launch_assign_gauss(dtype, D, X, wk.chat, wk.hb, N, K, B, lab, gsum, wk.part, sa, s), "gauss sum launch");
