@@ -197,7 +197,8 @@ def test_batched_equals_unbatched(km):
     assert torch.equal(l2, lb[0]) and torch.equal(C2, Cb[0])
 
 
-@pytest.mark.parametrize("n,k,batch", [(3001, 256, 7), (1025, 255, 7), (65_536, 200, 3), (70_001, 256, 2)])
+@pytest.mark.parametrize("n,k,batch", [(3001, 256, 7), (1025, 255, 7), (65_536, 200, 3), (70_001, 256, 2),
+                                       (5, 2, 300), (1, 1, 257)])
 def test_batched_update_skewed_labels(km, n, k, batch):
     """Batched update against the oracle, instance by instance.  With K <= 256
     the key sort takes one pass over tiles that stay inside an instance while
@@ -206,7 +207,9 @@ def test_batched_update_skewed_labels(km, n, k, batch):
     its own, 14 tiles where the unsegmented sort has 8; exactly 64 tiles in
     the third), and two passes beyond that (the fourth).  Labels: one
     instance entirely in the last cluster, one holding only the first and
-    last clusters, one Zipf-skewed, the rest uniform."""
+    last clusters, one Zipf-skewed, the rest uniform.  The last two cases are
+    hundreds of tiny instances (B*K above 256 with K <= 2): one nearly empty
+    tile per instance."""
     d = 64
     X, _, _, _ = datagen.mixture(n, d, 8, dtype="fp16", center_dist="normal", center_scale=2.0, sigma=1.0,
                                  weights=None, workload_code=57, seed=n, batch=batch)
