@@ -78,11 +78,12 @@ __device__ __forceinline__ TilePos tile_pos_t(int64_t g, int64_t n, const Segs& 
   }
 }
 
-// Mask of the active lanes of this wave whose 8-bit digit equals mine.
+// Mask of the active lanes of this wave whose RB-bit digit equals mine.
+template <int RB>
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
   uint64_t m = __ballot(valid);
 #pragma unroll
-  for (int bit = 0; bit < 8; ++bit) {
+  for (int bit = 0; bit < RB; ++bit) {
     const bool on = (d >> bit) & 1u;
     const uint64_t bb = __ballot(on);
     m &= on ? bb : ~bb;
@@ -96,17 +97,21 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
 // SEG: the n elements are consecutive segments of segN, each cut into ntb
 // tiles of its own (the last one ragged), and the digit is taken from
 // key - segment * kseg, so one pass sorts every segment by its local key.
-template <class Src, int TILE, bool SEG>
+// RB: digit bits (8, or up to 11 for a key sorted in one wide pass).
+template <class Src, int TILE, bool SEG, int RB = 8>
 __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int shift, uint32_t* __restrict__ hist,
                                                         int64_t nblk, int64_t dstride, int64_t tstride,
                                                         Segs seg, InertiaJob side) {
+  constexpr uint32_t R = 1u << RB;
+  constexpr int DPT = (int)R / kT;  // digits per thread
   if ((int64_t)blockIdx.x >= nblk) {
     inertia_reduce_block(side.part, side.nwg, (int64_t)blockIdx.x - nblk, side.inertia, side.hist, false);
     return;
   }
-  __shared__ uint32_t cnt[256];
+  __shared__ uint32_t cnt[R];
   const int t = threadIdx.x;
-  cnt[t] = 0;
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) cnt[t + kT * j] = 0;
   __syncthreads();
   const int64_t tile = xcd_tile(blockIdx.x, nblk);
   const TilePos p = tile_pos_t<SEG, TILE>(tile, n, seg);
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
 #pragma unroll
   for (int r = 0; r < kIPT; ++r) {
     const int64_t li = p.first + r * kT + t;
-    d[r] = li < p.lim ? ((src(p.row0 + li).x - p.koff) >> shift) & 255u : 256u;
+    d[r] = li < p.lim ? ((src(p.row0 + li).x - p.koff) >> shift) & (R - 1) : R;
   }
   // LDS atomics: the counts are exact integers, so their order is irrelevant.
   // When all 64 keys of a wave's round share one digit (a skewed label
@@ -126,13 +131,14 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
   for (int r = 0; r < kIPT; ++r) {
     const uint32_t d0 = __builtin_amdgcn_readfirstlane(d[r]);
     if (__ballot(d[r] == d0) == ~0ull) {
-      if (lane == 0 && d0 < 256u) atomicAdd(&cnt[d0], 64u);
-    } else if (d[r] < 256u) {
+      if (lane == 0 && d0 < R) atomicAdd(&cnt[d0], 64u);
+    } else if (d[r] < R) {
       atomicAdd(&cnt[d[r]], 1u);
     }
   }
   __syncthreads();
-  hist[(int64_t)t * dstride + tile * tstride] = cnt[t];
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) hist[(int64_t)(t + kT * j) * dstride + tile * tstride] = cnt[t + kT * j];
 }
 
 // One workgroup per digit: exclusive scan of hist[d][0..nblk) in place,
@@ -180,18 +186,24 @@ __global__ __launch_bounds__(kT) void radix_scan_kernel(uint32_t* __restrict__ h
 // run, so consecutive threads write consecutive addresses.
 // SEG (scan-free only): the tile sums the counts of its own segment's tiles
 // and writes into that segment's part of the output.
-template <class Src, int TILE, bool SCANNED, bool SEG>
+// RB > 8 (scanned only): a wide digit of up to 11 bits, so a key of that
+// many bits is sorted in one pass; thread t then owns the DPT consecutive
+// digits t*DPT .. t*DPT + DPT - 1 (with 8 bits, digit t).
+template <class Src, int TILE, bool SCANNED, bool SEG, int RB = 8>
 __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, int shift,
                                                            const uint32_t* __restrict__ hist,
                                                            const uint32_t* __restrict__ dtot, int64_t nblk,
                                                            Segs seg, uint2* __restrict__ out) {
   static_assert(!(SCANNED && SEG), "a segmented pass sums its own counts");
+  static_assert(RB == 8 || (SCANNED && !SEG), "wide digits use the scanned histogram");
+  constexpr uint32_t R = 1u << RB;
+  constexpr int DPT = (int)R / kT;    // digits per thread
   constexpr int KW = TILE / 4;        // keys per wave
   constexpr int RW = KW / 64;         // rounds per wave
   __shared__ uint2 lkv[TILE];
-  __shared__ uint32_t gbase[256];     // global position of LDS slot 0 of digit d's run, minus lstart[d]
-  __shared__ uint32_t lstart[256];    // first LDS slot of digit d
-  __shared__ uint32_t wcnt[4][256];   // per-wave digit counts, then per-wave offsets
+  __shared__ uint32_t gbase[R];       // global position of LDS slot 0 of digit d's run, minus lstart[d]
+  __shared__ uint32_t lstart[R];      // first LDS slot of digit d
+  __shared__ uint32_t wcnt[4][R];     // per-wave digit counts, then per-wave offsets
   __shared__ uint32_t tmp[4];
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
@@ -211,13 +223,20 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
     e[r] = li < p.lim ? src(p.row0 + li) : make_uint2(0u, 0u);
   }
 
-  // this tile's count of digit t: from the scanned (exclusive) histogram
-  // row, or summed here from the raw counts of the segment's tiles
-  uint32_t h0, h1, dt_t;
+  // this tile's first position among, and count of, each digit it owns
+  // (h0[j], cn[j]) and the digit's total (dt[j]): from the scanned
+  // (exclusive) histogram rows, or summed here from the raw counts of the
+  // segment's tiles
+  uint32_t h0[DPT], cn[DPT], dt[DPT];
   if constexpr (SCANNED) {
-    h0 = hist[(int64_t)t * nblk + blk];
-    h1 = blk + 1 < nblk ? hist[(int64_t)t * nblk + blk + 1] : dtot[t];
-    dt_t = dtot[t];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+      const int64_t d = (int64_t)t * DPT + j;
+      h0[j] = hist[d * nblk + blk];
+      const uint32_t h1 = blk + 1 < nblk ? hist[d * nblk + blk + 1] : dtot[d];
+      cn[j] = h1 - h0[j];
+      dt[j] = dtot[d];
+    }
   } else {
     // tile-major counts: tile j's count of digit t is hist[j * 256 + t]
     uint32_t c[kScanFreeTiles];
@@ -230,36 +249,50 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
       own += j == blk ? c[j] : 0u;
       all += c[j];
     }
-    h0 = before;
-    h1 = before + own;
-    dt_t = all;
+    h0[0] = before;
+    cn[0] = own;
+    dt[0] = all;
   }
-  uint32_t tot;
-  const uint32_t dpre = block_exclusive_scan_256(dt_t, tmp, &tot);
-  const uint32_t ls = block_exclusive_scan_256(h1 - h0, tmp, &tot);
-  lstart[t] = ls;
-  gbase[t] = (uint32_t)p.row0 + dpre + h0 - ls;
+  uint32_t sdt = 0, scn = 0;
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) wcnt[ww][t] = 0;
+  for (int j = 0; j < DPT; ++j) sdt += dt[j], scn += cn[j];
+  uint32_t tot;
+  uint32_t dpre = block_exclusive_scan_256(sdt, tmp, &tot);
+  uint32_t ls = block_exclusive_scan_256(scn, tmp, &tot);
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    const int d = t * DPT + j;
+    lstart[d] = ls;
+    gbase[d] = (uint32_t)p.row0 + dpre + h0[j] - ls;
+    dpre += dt[j];
+    ls += cn[j];
+  }
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww)
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) wcnt[ww][t * DPT + j] = 0;
   __syncthreads();
 
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const bool valid = first + r * 64 + lane < p.lim;
-    const uint32_t d = ((e[r].x - p.koff) >> shift) & 255u;
-    const uint64_t m = match_digit(d, valid);
+    const uint32_t d = ((e[r].x - p.koff) >> shift) & (R - 1);
+    const uint64_t m = match_digit<RB>(d, valid);
     const uint32_t lrank = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
     const uint32_t before = wcnt[w][d];
     rr[r] = before + lrank;
     if (valid && lrank == 0) wcnt[w][d] = before + (uint32_t)__popcll(m);
   }
   __syncthreads();
-  {  // per-wave counts -> exclusive per-wave offsets (thread t owns digit t)
+  // per-wave counts -> exclusive per-wave offsets (thread t owns its digits)
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    const int d = t * DPT + j;
     uint32_t run = 0;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const uint32_t c = wcnt[ww][t];
-      wcnt[ww][t] = run;
+      const uint32_t c = wcnt[ww][d];
+      wcnt[ww][d] = run;
       run += c;
     }
   }
@@ -267,7 +300,7 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     if (first + r * 64 + lane < p.lim) {
-      const uint32_t d = ((e[r].x - p.koff) >> shift) & 255u;
+      const uint32_t d = ((e[r].x - p.koff) >> shift) & (R - 1);
       lkv[lstart[d] + wcnt[w][d] + rr[r]] = e[r];
     }
   }
@@ -276,7 +309,7 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
   const int cnt = rem < TILE ? (int)rem : TILE;
   for (int i = t; i < cnt; i += kT) {
     const uint2 v = lkv[i];
-    out[gbase[((v.x - p.koff) >> shift) & 255u] + (uint32_t)i] = v;
+    out[gbase[((v.x - p.koff) >> shift) & (R - 1)] + (uint32_t)i] = v;
   }
 }
 
@@ -306,6 +339,26 @@ hipError_t one_pass(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out,
                                         : one_pass_t<Src, kSortTile>(src, n, shift, buf, out, s, side);
 }
 
+// One pass over keys of RB (9 to 11) bits with RB-bit digits: histogram,
+// one scan workgroup per digit, scatter.
+template <class Src, int TILE, int RB>
+hipError_t wide_pass_t(Src src, int64_t n, SortBuffers& buf, uint2* out, hipStream_t s, const InertiaJob& side) {
+  const int64_t nblk = (n + TILE - 1) / TILE;
+  const int64_t extra = side.part ? side.B : 0;
+  radix_hist_kernel<Src, TILE, false, RB><<<dim3((unsigned)(nblk + extra)), dim3(kT), 0, s>>>(
+      src, n, 0, buf.hist, nblk, nblk, 1, Segs{}, side);
+  radix_scan_kernel<<<dim3(1u << RB), dim3(kT), 0, s>>>(buf.hist, nblk, buf.dtot);
+  radix_scatter_kernel<Src, TILE, true, false, RB><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(
+      src, n, 0, buf.hist, buf.dtot, nblk, Segs{}, out);
+  return hipGetLastError();
+}
+
+template <int RB>
+hipError_t wide_pass(const LabelSrc& src, int64_t n, SortBuffers& buf, uint2* out, hipStream_t s,
+                     const InertiaJob& side) {
+  return wide_pass_t<LabelSrc, kSortTileSmall, RB>(src, n, buf, out, s, side);  // sort_wide_bits: small tiles only
+}
+
 // One segmented pass: B segments of N keys b*K + label with K <= 256, each
 // tiled on its own, ntb = ceil(N / TILE) <= kScanFreeTiles tiles per segment,
 // B * ntb tiles in all (the histogram holds sort_seg_blocks(N, B) tiles).
@@ -328,10 +381,7 @@ hipError_t seg_pass_t(const LabelSrc& src, int64_t N, int B, uint32_t K, SortBuf
 hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K, SortBuffers& buf,
                                  const uint2** sorted, hipStream_t s, const InertiaJob* side) {
   const int64_t n = N * (int64_t)B;
-  const uint64_t nseg = (uint64_t)B * (uint64_t)K;
-  int bits = 1;
-  while (bits < 32 && (1ull << bits) < nseg) ++bits;
-  const int passes = (bits + 7) / 8;
+  const int passes = (sort_key_bits(B, K) + 7) / 8;
   LabelSrc ls{labels, N, (uint32_t)K, B, 1.0 / (double)N};
   if (passes > 1 && sort_segmented(N, B, K)) {
     // instances arrive one after another, so sorting each by its label alone
@@ -340,6 +390,14 @@ hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K,
     return sort_tile(n) == kSortTileSmall
                ? seg_pass_t<kSortTileSmall>(ls, N, B, (uint32_t)K, buf, buf.kv[0], s, side ? *side : InertiaJob{})
                : seg_pass_t<kSortTile>(ls, N, B, (uint32_t)K, buf, buf.kv[0], s, side ? *side : InertiaJob{});
+  }
+  if (const int wb = sort_wide_bits(N, B, K)) {
+    // the whole key fits one digit of 9 to 11 bits: a single pass
+    *sorted = buf.kv[0];
+    const InertiaJob sj = side ? *side : InertiaJob{};
+    return wb == 9    ? wide_pass<9>(ls, n, buf, buf.kv[0], s, sj)
+           : wb == 10 ? wide_pass<10>(ls, n, buf, buf.kv[0], s, sj)
+                      : wide_pass<11>(ls, n, buf, buf.kv[0], s, sj);
   }
   hipError_t e = one_pass(ls, n, 0, buf, buf.kv[0], s, side ? *side : InertiaJob{});
   if (e != hipSuccess) return e;

@@ -41,8 +41,8 @@ inline Layout make_layout(int64_t N, int D, int K, int B, int dt) {
   L.cnt = o;   o = al256(o + (size_t)nseg * 4);
   L.kv0 = o;   o = al256(o + (size_t)n * 8);
   L.kv1 = o;   o = al256(o + (size_t)n * 8);
-  L.hist = o;  o = al256(o + (size_t)256 * sort_hist_tiles(N, B, K) * 4);
-  L.dtot = o;  o = al256(o + 256 * 4);
+  L.hist = o;  o = al256(o + (size_t)sort_hist_words(N, B, K) * 4);
+  L.dtot = o;  o = al256(o + ((size_t)1 << kSortWideBits) * 4);
   L.off = o;   o = al256(o + (size_t)(nseg + 1) * 4);
   L.frag = o;  o = al256(o + (size_t)seg_chunks(n) * 2 * D * 4);
   L.gfrag = o; o = al256(o + (size_t)seg_groups(n) * 2 * D * 8);

@@ -231,6 +231,32 @@ def test_batched_update_skewed_labels(km, n, k, batch):
     H.log(f"batched update n={n} k={k} B={batch}: worst centroid err {worst:.2e}")
 
 
+@pytest.mark.parametrize("n,k,batch", [(20_011, 257, 1), (50_000, 2048, 1), (30_001, 300, 2), (9_001, 290, 7)])
+def test_wide_digit_update(km, n, k, batch):
+    """Keys of 9 to 11 bits (B*K from 257 to 2048) sort in one pass with a
+    digit that wide while its histogram stays within 2^20 words: 9 and 11
+    bits unbatched, 10 and 11 bits over instances whose K is too large for
+    the segmented pass.  Skewed labels (one instance all in the last
+    cluster, one Zipf) against the oracle."""
+    d = 32
+    X, _, _, _ = datagen.mixture(n, d, 8, dtype="bf16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                 weights=None, workload_code=58, seed=k, batch=batch)
+    rng = np.random.default_rng(n)
+    lab = rng.integers(0, k, size=(batch, n)).astype(np.int32)
+    lab[0, : n // 3] = k - 1
+    if batch > 1:
+        lab[1] = datagen.zipf_labels(n, k, 1.1, seed=5)[0]
+    C_prev = torch.randn(batch, k, d, generator=torch.Generator().manual_seed(7))
+    C_new, counts = km.update(X.cuda(), torch.from_numpy(lab).cuda(), C_prev.cuda())
+    torch.cuda.synchronize()
+    C_new, counts = C_new.cpu().numpy(), counts.cpu().numpy()
+    worst = 0.0
+    for b in range(batch):
+        worst = max(worst, H.check_update(H.decode(X[b], "bf16"), lab[b], C_prev[b].numpy(), C_new[b], counts[b], k,
+                                          tag=f"wide n={n} k={k} b={b}"))
+    H.log(f"wide-digit update n={n} k={k} B={batch}: worst centroid err {worst:.2e}")
+
+
 def test_determinism_and_resume(km):
     p = datagen.make("c3", n=50000, k=777, seed=6)
     X, C0 = p.X.cuda(), p.C0.cuda()
