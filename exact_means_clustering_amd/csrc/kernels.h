@@ -146,7 +146,8 @@ inline int64_t sort_hist_words(int64_t N, int B, int K) {
 // reads and writes each element with a single access.
 struct SortBuffers {
   uint2* kv[2];     // [n] each: ping-pong pair buffers
-  uint32_t* hist;   // [sort_hist_words(N, B, K)]
+  uint32_t* hist;   // [hist_words], at least sort_hist_words(N, B, K) for the shape it was laid out for
+  int64_t hist_words;  // capacity of hist: a call takes only a pass whose histogram fits
   uint32_t* dtot;   // [2^kSortWideBits] digit totals
 };
 // Sorts rows by key = b*K + clamp(labels[b*N+i], 0, K-1) (stable).  On return

@@ -383,7 +383,13 @@ hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K,
   const int64_t n = N * (int64_t)B;
   const int passes = (sort_key_bits(B, K) + 7) / 8;
   LabelSrc ls{labels, N, (uint32_t)K, B, 1.0 / (double)N};
-  if (passes > 1 && sort_segmented(N, B, K)) {
+  // A workspace laid out for more rows than this call sorts (the streamed
+  // path's last chunk) may not hold the histogram of the one-pass variants,
+  // whose size is not monotone in the row count: they are taken only if the
+  // histogram fits, and the plain passes always fit a layout for at least n.
+  const int64_t T = sort_tile(n);
+  const bool seg_fits = 256 * ((N + T - 1) / T) * (int64_t)B <= buf.hist_words;
+  if (passes > 1 && sort_segmented(N, B, K) && seg_fits) {
     // instances arrive one after another, so sorting each by its label alone
     // gives the order of the key b*K + label in one pass
     *sorted = buf.kv[0];
@@ -391,7 +397,8 @@ hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K,
                ? seg_pass_t<kSortTileSmall>(ls, N, B, (uint32_t)K, buf, buf.kv[0], s, side ? *side : InertiaJob{})
                : seg_pass_t<kSortTile>(ls, N, B, (uint32_t)K, buf, buf.kv[0], s, side ? *side : InertiaJob{});
   }
-  if (const int wb = sort_wide_bits(N, B, K)) {
+  const int wb = sort_wide_bits(N, B, K);
+  if (wb && ((int64_t)1 << wb) * sort_blocks(n) <= buf.hist_words) {
     // the whole key fits one digit of 9 to 11 bits: a single pass
     *sorted = buf.kv[0];
     const InertiaJob sj = side ? *side : InertiaJob{};
@@ -399,6 +406,7 @@ hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K,
            : wb == 10 ? wide_pass<10>(ls, n, buf, buf.kv[0], s, sj)
                       : wide_pass<11>(ls, n, buf, buf.kv[0], s, sj);
   }
+  if (256 * sort_blocks(n) > buf.hist_words) return hipErrorInvalidValue;  // workspace laid out for fewer rows
   hipError_t e = one_pass(ls, n, 0, buf, buf.kv[0], s, side ? *side : InertiaJob{});
   if (e != hipSuccess) return e;
   int cur = 0;

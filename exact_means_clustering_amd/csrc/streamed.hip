@@ -102,15 +102,24 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
     lslot[i] = (int32_t*)r.alloc(al256((size_t)chunk * 4));
     if (!xslot[i] || !lslot[i]) return bad(KM_ENOMEM, "device slot allocation failed");
   }
-  const size_t ws_bytes = make_layout(chunk > K ? chunk : K, D, K, 1, dtype).total;
+  // Every chunk but the last has `chunk` rows.  The workspace is laid out
+  // for each of the two row counts (sort tiles and segment chunks change
+  // size at 2^21 rows, so a layout for more rows need not cover fewer) in
+  // one allocation of the larger size; a chunk uses its own layout.  The
+  // stages of one chunk run in order on the compute stream, so the two
+  // carvings never hold live data at once, and the centroid preparation
+  // sits at the same offsets in both.
+  const int64_t last = N - (nch - 1) * chunk;
+  const Layout LF = make_layout(chunk, D, K, 1, dtype), LL = make_layout(last, D, K, 1, dtype);
+  const size_t ws_bytes = LF.total > LL.total ? LF.total : LL.total;
   void* ws = r.alloc(ws_bytes);
   double* S_acc = (double*)r.alloc((size_t)K * D * 8);
   int64_t* n_acc = (int64_t*)r.alloc((size_t)K * 8);
   double* J_dev = (double*)r.alloc((size_t)iters * 8);
   if (!ws || !S_acc || !n_acc || !J_dev) return bad(KM_ENOMEM, "device workspace allocation failed");
 
-  const int64_t wsN = chunk > K ? chunk : K;
-  Work w = carve(ws, make_layout(wsN, D, K, 1, dtype));
+  Work wf = carve(ws, LF), wl = carve(ws, LL);
+  Work& w = wf;  // centroid preparation and partials: same offsets in both layouts
 
   const char* xh = (const char*)X_host;
   // both slots start free
@@ -137,18 +146,19 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
     for (int64_t c = 0; c < nch; ++c) {
       const int sl = (int)(c & 1);
       const int64_t rows = (c + 1) * chunk <= N ? chunk : N - c * chunk;
+      Work& wc = rows == chunk ? wf : wl;
       if (c + 1 < nch)
         if (int rc = h2d(c + 1)) return rc;
       KS_HIP(hipStreamWaitEvent(r.cs, r.copied[sl], 0), "stream wait");
       const AssignConfig cfg = assign_pick(dtype, D, rows, 1, K);
-      KS_HIP(launch_assign(dtype, D, cfg, xslot[sl], w.chat, w.hb, rows, K, 1, lslot[sl], nullptr, w.part, r.cs),
+      KS_HIP(launch_assign(dtype, D, cfg, xslot[sl], wc.chat, wc.hb, rows, K, 1, lslot[sl], nullptr, wc.part, r.cs),
              "assign launch");
       const int64_t nwg = (rows + cfg.rows() - 1) / cfg.rows();
-      KS_HIP(launch_inertia_reduce(w.part, (int)nwg, 1, J_dev + t, nullptr, true, r.cs), "inertia launch");
+      KS_HIP(launch_inertia_reduce(wc.part, (int)nwg, 1, J_dev + t, nullptr, true, r.cs), "inertia launch");
       const uint2* sorted = nullptr;
-      KS_HIP(launch_argsort_labels(lslot[sl], rows, 1, K, w.sort, &sorted, r.cs), "argsort launch");
+      KS_HIP(launch_argsort_labels(lslot[sl], rows, 1, K, wc.sort, &sorted, r.cs), "argsort launch");
       SegOut so{nullptr, nullptr, nullptr, S_acc, n_acc};
-      KS_HIP(launch_segment_reduce(dtype, D, xslot[sl], sorted, w.off, rows, (uint32_t)K, so, w.seg, r.cs),
+      KS_HIP(launch_segment_reduce(dtype, D, xslot[sl], sorted, wc.off, rows, (uint32_t)K, so, wc.seg, r.cs),
              "segment reduce launch");
       KS_HIP(hipEventRecord(r.done[sl], r.cs), "event record");
       KS_HIP(hipStreamWaitEvent(r.xs, r.done[sl], 0), "stream wait");

@@ -72,6 +72,7 @@ inline Work carve(void* ws, const Layout& L) {
   w.sort.kv[0] = reinterpret_cast<uint2*>(at(L.kv0));
   w.sort.kv[1] = reinterpret_cast<uint2*>(at(L.kv1));
   w.sort.hist = reinterpret_cast<uint32_t*>(at(L.hist));
+  w.sort.hist_words = (int64_t)((L.dtot - L.hist) / 4);
   w.sort.dtot = reinterpret_cast<uint32_t*>(at(L.dtot));
   w.off = reinterpret_cast<int32_t*>(at(L.off));
   w.seg.frag = reinterpret_cast<float*>(at(L.frag));

@@ -310,6 +310,31 @@ def test_streamed_matches_in_core(km):
     H.check_assign(Xd, C_prev.cpu().numpy(), lab_s.numpy(), J_s, "fp16", tag="streamed")
 
 
+@pytest.mark.parametrize("last", [500_000, 2_000_000])
+def test_streamed_last_chunk_across_the_tile_size_change(km, last):
+    """Slots of just over 2^21 rows and a last chunk of fewer: sort tiles and
+    segment chunks are smaller up to 2^21 rows, so the last chunk needs a
+    workspace layout of its own (at 500,000 rows its K = 1024 keys also take
+    the one-pass wide-digit sort).  Streamed against in-core."""
+    chunk, d, k = 2_097_152 + 1000, 16, 1024
+    n = chunk + last
+    X, C0, _, _ = datagen.mixture(n, d, 64, dtype="fp16", center_dist="normal", center_scale=3.0, sigma=1.0,
+                                  weights=None, workload_code=63, seed=last, k=k)
+    X, C0 = X[0], C0[0]
+    budget = 2 * chunk * d * 2                      # two slots of `chunk` rows: two chunks
+    lab_s, C_s, J_s, hist_s = km.fit_streamed(X.pin_memory(), C0.cuda(), 2, budget, history=True)
+    lab_i, C_i, J_i, hist_i = km.fit(X.cuda(), C0.cuda(), 2, history=True)
+    torch.cuda.synchronize()
+    assert abs(hist_s[0] - float(hist_i[0, 0])) <= 1e-9 * hist_s[0]
+    assert abs(J_s - float(J_i[0])) <= 1e-5 * J_s
+    Xd = H.decode(X, "fp16")
+    rms = float(np.sqrt(np.einsum("ij,ij->i", Xd, Xd).mean()))
+    import oracle
+    assert oracle.centroid_rel_err(C_s.cpu().numpy(), C_i.cpu().numpy(), rms) <= 1e-4
+    mism = int((lab_s != lab_i.cpu()).sum())
+    assert mism <= 1e-4 * n, mism
+
+
 @pytest.mark.slow
 def test_c4_full(km):
     p = datagen.make("c4")
