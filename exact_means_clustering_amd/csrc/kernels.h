@@ -102,9 +102,13 @@ inline int64_t sort_blocks(int64_t n) { return (n + sort_tile(n) - 1) / sort_til
 // covers at most this many tiles (per segment, for a segmented pass).
 constexpr int64_t kScanFreeTiles = 64;
 // B > 1 instances with K <= 256 sort in one segmented pass (each instance by
-// its label) when an instance spans at most kScanFreeTiles tiles.
+// its label) when an instance spans at most kScanFreeTiles tiles and the
+// per-instance tiles number at most twice the plain ones (tiles at least
+// half full on average, so many tiny instances keep the plain passes and a
+// histogram that grows with the keys, not with the instance count).
 inline bool sort_segmented(int64_t N, int B, int K) {
-  return B > 1 && K <= 256 && (N + sort_tile(N * B) - 1) / sort_tile(N * B) <= kScanFreeTiles;
+  const int64_t ntb = (N + sort_tile(N * B) - 1) / sort_tile(N * B);
+  return B > 1 && K <= 256 && ntb <= kScanFreeTiles && ntb * B <= 2 * sort_blocks(N * B);
 }
 // Tiles the sort's histogram must hold: a segmented pass tiles each
 // instance separately, so its ragged tails can add up to B - 1 tiles.

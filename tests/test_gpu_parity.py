@@ -208,8 +208,9 @@ def test_batched_update_skewed_labels(km, n, k, batch):
     the third), and two passes beyond that (the fourth).  Labels: one
     instance entirely in the last cluster, one holding only the first and
     last clusters, one Zipf-skewed, the rest uniform.  The last two cases are
-    hundreds of tiny instances (B*K above 256 with K <= 2): one nearly empty
-    tile per instance."""
+    hundreds of tiny instances (B*K of 600 and 257 with K <= 2), which do not
+    take the segmented pass (it would need a nearly empty tile per instance)
+    but the one-pass wide-digit sort of their 10- and 9-bit keys."""
     d = 64
     X, _, _, _ = datagen.mixture(n, d, 8, dtype="fp16", center_dist="normal", center_scale=2.0, sigma=1.0,
                                  weights=None, workload_code=57, seed=n, batch=batch)
