@@ -122,16 +122,18 @@ def test_forced_empty_clusters(km):
     assert torch.equal(C.cpu()[0, 5], C0[0, 5]) and torch.equal(C.cpu()[0, 17], C0[0, 17])
 
 
-@pytest.mark.parametrize("dtype,d,batch", [("bf16", 128, 2), ("fp32", 32, 1), ("fp16", 64, 3)])
-def test_fit_equals_stepwise_calls(km, dtype, d, batch):
+@pytest.mark.parametrize("dtype,d,batch,k", [("bf16", 128, 2, 33), ("fp32", 32, 1, 33), ("fp16", 64, 3, 33),
+                                             ("fp16", 64, 3, 300), ("bf16", 64, 5, 120)])
+def test_fit_equals_stepwise_calls(km, dtype, d, batch, k):
     """kmeans_fit folds the inertia reduction into the sort and the next
     iteration's centroid preparation into the update (empty clusters keep the
     preparation of their unchanged centroid).  Its labels, centroids and
     inertia history must equal the same iterations run as stand-alone
     kmeans_assign + kmeans_update calls bit for bit, with empty clusters
-    present in every instance."""
+    present in every instance.  The sort takes one 8-bit pass for K = 33, the
+    wide-digit pass for 3 x 300 keys and the segmented pass for 5 x 120."""
     X, C0, _, _ = datagen.mixture(12_345, d, 20, dtype=dtype, center_dist="normal", center_scale=2.0, sigma=1.0,
-                                  weights=None, workload_code=57, seed=3, k=33, batch=batch)
+                                  weights=None, workload_code=57, seed=3, k=k, batch=batch)
     C0 = C0.clone()
     C0[:, 4] = 1e4            # far away: empty in every iteration of every instance
     C0[:, 30] = -1e4
