@@ -71,6 +71,13 @@ def test_workspace_bytes(lib):
     # the workspace holds no O(N*K) buffer: it grows linearly in N and K
     big = lib.kmeans_workspace_bytes(1 << 23, 128, 65536, 1, 2)
     assert big < 64 * (1 << 23) + 1024 * 65536
+    # a million one-row instances: the sort histogram grows with the keys, not
+    # with the instance count (no per-instance sort tile).  The two bias /
+    # weight arrays are padded to a 256-centroid tile per instance
+    # (2 * B * 256 * 4 bytes); everything else stays in the hundreds of MB.
+    B = 1 << 20
+    tiny = lib.kmeans_workspace_bytes(1, 32, 1, B, 0)
+    assert 0 < tiny - 2 * B * 256 * 4 < 400 * (1 << 20)
 
 
 FAKE = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first
