@@ -20,7 +20,8 @@
 // tile-major and each scatter workgroup sums the counts it needs.  Batched
 // keys with K <= 256 take a single segmented pass: the instances arrive one
 // after another, so tiles that stay inside one instance and sort by the label
-// alone produce the order of b*K + label.
+// alone produce the order of b*K + label.  Other keys of 9 to 11 bits take a
+// single pass whose digit is the whole key (2^bits counts per tile).
 #include "common.h"
 #include "kernels.h"
 
