@@ -14,6 +14,7 @@ centroids are [K, D] or [B, K, D] fp32.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -107,13 +108,41 @@ def _dtype(X):
         raise KMeansError(KM_EUNSUPPORTED, f"unsupported dtype {X.dtype}") from None
 
 
-def _need(t, name, dtype=None):
+def _need(t, name, dtype=None, like=None):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise KMeansError(KM_EINVAL, f"{name} must be a CUDA tensor")
     if not t.is_contiguous():
         raise KMeansError(KM_EINVAL, f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise KMeansError(KM_EINVAL, f"{name} must be {dtype}")
+    if like is not None and t.device != like.device:
+        raise KMeansError(KM_EINVAL, f"{name} must be on {like.device} (it is on {t.device})")
+
+
+def _on_tensor_device(fn):
+    """Run fn with its first CUDA tensor argument's device current, so the
+    default stream and the library's device queries belong to that device."""
+    @functools.wraps(fn)
+    def run(*args, **kwargs):
+        for a in args:
+            if isinstance(a, torch.Tensor) and a.is_cuda:
+                with torch.cuda.device(a.device):
+                    return fn(*args, **kwargs)
+        return fn(*args, **kwargs)
+    return run
+
+
+def _rows(C, name, B, D):
+    """K of a centroid-like tensor [K, D] (B = 1) or [B, K, D] that goes with X."""
+    ok = C.shape[-1] == D and (C.dim() == 3 and C.shape[0] == B or C.dim() == 2 and B == 1)
+    if not ok:
+        raise KMeansError(KM_EINVAL, f"{name} must be [K, {D}] or [{B}, K, {D}] (got {tuple(C.shape)})")
+    return C.shape[-2]
+
+
+def _count(t, name, n):
+    if t.numel() != n:
+        raise KMeansError(KM_EINVAL, f"{name} must have {n} elements (got {t.numel()})")
 
 
 def workspace_bytes(N: int, D: int, K: int, B: int = 1, dtype=torch.bfloat16) -> int:
@@ -122,87 +151,104 @@ def workspace_bytes(N: int, D: int, K: int, B: int = 1, dtype=torch.bfloat16) ->
 
 
 def _workspace(N, D, K, B, dt, device, ws):
+    """A caller workspace (any dtype, contiguous, on X's device) or a new one;
+    returns (tensor, its size in bytes)."""
     need = int(_lib.kmeans_workspace_bytes(N, D, K, B, dt))
     if need == 0:
         _check(_lib.kmeans_workspace_bytes(N, D, K, B, dt) or KM_EINVAL)
-    if ws is None or ws.numel() < need:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
-    return ws
+    if ws is not None:
+        if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+            raise KMeansError(KM_EINVAL, f"ws must be a contiguous tensor on {device}")
+        if ws.numel() * ws.element_size() >= need:
+            return ws, ws.numel() * ws.element_size()
+    return torch.empty(need, dtype=torch.uint8, device=device), need
 
 
+@_on_tensor_device
 def assign(X, C, *, want_min_d2: bool = False, ws=None, stream=None, labels=None):
     """Assignment stage: returns (labels int32, min_d2 fp32 or None, inertia fp64 [B])."""
     _need(X, "X")
-    _need(C, "C", torch.float32)
+    _need(C, "C", torch.float32, like=X)
     B, N, D = _shape3(X)
-    K = C.shape[-2]
+    K = _rows(C, "C", B, D)
     dt = _dtype(X)
     lab_shape = X.shape[:-1]
-    labels = torch.empty(lab_shape, dtype=torch.int32, device=X.device) if labels is None else labels
+    if labels is None:
+        labels = torch.empty(lab_shape, dtype=torch.int32, device=X.device)
+    else:
+        _need(labels, "labels", torch.int32, like=X)
+        _count(labels, "labels", B * N)
     md = torch.empty(lab_shape, dtype=torch.float32, device=X.device) if want_min_d2 else None
     inertia = torch.empty(B, dtype=torch.float64, device=X.device)
-    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    ws, ws_bytes = _workspace(N, D, K, B, dt, X.device, ws)
     _check(_lib.kmeans_assign(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(labels), _ptr(md), _ptr(inertia),
-                              _ptr(ws), ws.numel(), _stream(stream)))
+                              _ptr(ws), ws_bytes, _stream(stream)))
     return labels, md, inertia
 
 
+@_on_tensor_device
 def assign_top2(X, C, *, ws=None, stream=None):
     """Two nearest centroids of every point: returns (labels [.., N, 2] int32, distances [.., N, 2] fp32)."""
     _need(X, "X")
-    _need(C, "C", torch.float32)
+    _need(C, "C", torch.float32, like=X)
     B, N, D = _shape3(X)
-    K = C.shape[-2]
+    K = _rows(C, "C", B, D)
     dt = _dtype(X)
     labels2 = torch.empty((*X.shape[:-1], 2), dtype=torch.int32, device=X.device)
     d2 = torch.empty((*X.shape[:-1], 2), dtype=torch.float32, device=X.device)
-    ws = _workspace(N, D, K, B, dt, X.device, ws)
-    _check(_lib.kmeans_assign_top2(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(labels2), _ptr(d2), _ptr(ws), ws.numel(),
+    ws, ws_bytes = _workspace(N, D, K, B, dt, X.device, ws)
+    _check(_lib.kmeans_assign_top2(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(labels2), _ptr(d2), _ptr(ws), ws_bytes,
                                    _stream(stream)))
     return labels2, d2
 
 
+@_on_tensor_device
 def assign_soft(X, C, sigma2: float, *, log_w=None, ws=None, stream=None):
     """Gaussian-mixture soft assignment (shared variance sigma2, log-weights log_w [.., K] or None): returns
     (most responsible component int32, log density fp32, its per-instance sum fp64 [B])."""
     _need(X, "X")
-    _need(C, "C", torch.float32)
+    _need(C, "C", torch.float32, like=X)
     if log_w is not None:
-        _need(log_w, "log_w", torch.float32)
+        _need(log_w, "log_w", torch.float32, like=X)
     B, N, D = _shape3(X)
-    K = C.shape[-2]
+    K = _rows(C, "C", B, D)
+    if log_w is not None:
+        _count(log_w, "log_w", B * K)
     dt = _dtype(X)
     labels = torch.empty(X.shape[:-1], dtype=torch.int32, device=X.device)
     logp = torch.empty(X.shape[:-1], dtype=torch.float32, device=X.device)
     total = torch.empty(B, dtype=torch.float64, device=X.device)
-    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    ws, ws_bytes = _workspace(N, D, K, B, dt, X.device, ws)
     _check(_lib.kmeans_assign_soft(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(log_w), float(sigma2), _ptr(labels),
-                                   _ptr(logp), _ptr(total), _ptr(ws), ws.numel(), _stream(stream)))
+                                   _ptr(logp), _ptr(total), _ptr(ws), ws_bytes, _stream(stream)))
     return labels, logp, total
 
 
+@_on_tensor_device
 def gauss_sum(X, Y, w, sigma2: float, *, ws=None, stream=None):
     """Gauss kernel sums G[.., i] = sum_k w[.., k] exp(-||x_i - y_k||^2 / (2 sigma2)): returns (G fp32, sum fp64 [B])."""
     _need(X, "X")
-    _need(Y, "Y", torch.float32)
-    _need(w, "w", torch.float32)
+    _need(Y, "Y", torch.float32, like=X)
+    _need(w, "w", torch.float32, like=X)
     B, N, D = _shape3(X)
-    K = Y.shape[-2]
+    K = _rows(Y, "Y", B, D)
+    _count(w, "w", B * K)
     dt = _dtype(X)
     G = torch.empty(X.shape[:-1], dtype=torch.float32, device=X.device)
     total = torch.empty(B, dtype=torch.float64, device=X.device)
-    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    ws, ws_bytes = _workspace(N, D, K, B, dt, X.device, ws)
     _check(_lib.kmeans_gauss_sum(_ptr(X), dt, N, D, B, _ptr(Y), K, _ptr(w), float(sigma2), _ptr(G), _ptr(total),
-                                 _ptr(ws), ws.numel(), _stream(stream)))
+                                 _ptr(ws), ws_bytes, _stream(stream)))
     return G, total
 
 
+@_on_tensor_device
 def seed(X, u, *, method: str = "kmeans++", want_d2: bool = False, ws=None, stream=None):
     """Initial centroids from the caller's uniforms u [.., K] (fp64, CUDA, in [0, 1)): method "random" (rows
     floor(u N)) or "kmeans++" (D^2 sampling).  Returns (row indices int32 [.., K], centroids fp32 [.., K, D],
     squared distance of every row to its nearest pick fp32 [.., N] or None)."""
     _need(X, "X")
-    _need(u, "u", torch.float64)
+    _need(u, "u", torch.float64, like=X)
     B, N, D = _shape3(X)
     K = u.shape[-1]
     if u.numel() != B * K:
@@ -214,49 +260,56 @@ def seed(X, u, *, method: str = "kmeans++", want_d2: bool = False, ws=None, stre
     idx = torch.empty(u.shape, dtype=torch.int32, device=X.device)
     C = torch.empty((*u.shape, D), dtype=torch.float32, device=X.device)
     d2 = torch.empty(X.shape[:-1], dtype=torch.float32, device=X.device) if want_d2 else None
-    ws = _workspace(N, D, K, B, dt, X.device, ws)
-    _check(_lib.kmeans_seed(_ptr(X), dt, N, D, B, K, m, _ptr(u), _ptr(idx), _ptr(C), _ptr(d2), _ptr(ws), ws.numel(),
+    ws, ws_bytes = _workspace(N, D, K, B, dt, X.device, ws)
+    _check(_lib.kmeans_seed(_ptr(X), dt, N, D, B, K, m, _ptr(u), _ptr(idx), _ptr(C), _ptr(d2), _ptr(ws), ws_bytes,
                             _stream(stream)))
     return idx, C, d2
 
 
+@_on_tensor_device
 def update(X, labels, C_prev, *, C_new=None, ws=None, stream=None):
     """Centroid update stage: returns (C_new fp32, counts int32)."""
     _need(X, "X")
-    _need(labels, "labels", torch.int32)
-    _need(C_prev, "C_prev", torch.float32)
+    _need(labels, "labels", torch.int32, like=X)
+    _need(C_prev, "C_prev", torch.float32, like=X)
     B, N, D = _shape3(X)
-    K = C_prev.shape[-2]
+    K = _rows(C_prev, "C_prev", B, D)
+    _count(labels, "labels", B * N)
     dt = _dtype(X)
-    C_new = torch.empty_like(C_prev) if C_new is None else C_new
+    if C_new is None:
+        C_new = torch.empty_like(C_prev)
+    else:
+        _need(C_new, "C_new", torch.float32, like=X)
+        _count(C_new, "C_new", B * K * D)
     counts = torch.empty(C_prev.shape[:-1], dtype=torch.int32, device=X.device)
-    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    ws, ws_bytes = _workspace(N, D, K, B, dt, X.device, ws)
     _check(_lib.kmeans_update(_ptr(X), dt, N, D, B, _ptr(labels), K, _ptr(C_prev), _ptr(C_new), _ptr(counts),
-                              _ptr(ws), ws.numel(), _stream(stream)))
+                              _ptr(ws), ws_bytes, _stream(stream)))
     return C_new, counts
 
 
+@_on_tensor_device
 def fit(X, C0, iters: int, *, history: bool = False, ws=None, stream=None, out=None):
     """Exact Lloyd iteration: returns (labels, C, inertia [B] fp64, history [iters, B] or None).
 
     ``out`` = (labels, C, inertia, history-or-None) reuses caller tensors for the results: calls with the same
     buffers replay the library's captured graph of the fit instead of capturing a new one."""
     _need(X, "X")
-    _need(C0, "C0", torch.float32)
+    _need(C0, "C0", torch.float32, like=X)
     B, N, D = _shape3(X)
-    K = C0.shape[-2]
+    K = _rows(C0, "C0", B, D)
     dt = _dtype(X)
     if out is not None:
         labels, C, inertia, hist = out
-        _need(labels, "labels", torch.int32)
-        _need(C, "C", torch.float32)
-        _need(inertia, "inertia", torch.float64)
+        _need(labels, "labels", torch.int32, like=X)
+        _need(C, "C", torch.float32, like=X)
+        _need(inertia, "inertia", torch.float64, like=X)
         if labels.numel() != B * N or C.numel() != B * K * D or inertia.numel() != B:
             raise KMeansError(KM_EINVAL, "out tensors do not match the problem's shapes")
         if history:
             if hist is None or hist.numel() < max(1, int(iters)) * B:
                 raise KMeansError(KM_EINVAL, "history requested but out[3] is missing or too small")
-            _need(hist, "history", torch.float64)
+            _need(hist, "history", torch.float64, like=X)
         else:
             hist = None
     else:
@@ -264,24 +317,29 @@ def fit(X, C0, iters: int, *, history: bool = False, ws=None, stream=None, out=N
         C = torch.empty_like(C0)
         inertia = torch.empty(B, dtype=torch.float64, device=X.device)
         hist = torch.empty((max(1, int(iters)), B), dtype=torch.float64, device=X.device) if history else None
-    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    ws, ws_bytes = _workspace(N, D, K, B, dt, X.device, ws)
     _check(_lib.kmeans_fit(_ptr(X), dt, N, D, B, _ptr(C0), K, int(iters), _ptr(labels), _ptr(C), _ptr(inertia),
-                           _ptr(hist), _ptr(ws), ws.numel(), _stream(stream)))
+                           _ptr(hist), _ptr(ws), ws_bytes, _stream(stream)))
     return labels, C, inertia, hist
 
 
+@_on_tensor_device
 def tune(X, C, *, labels=None, ws=None, stream=None):
     """Time every compiled assignment configuration on this shape and record the
     fastest in the library's tuning table.  Returns (pb, waves, ms per launch)."""
     _need(X, "X")
-    _need(C, "C", torch.float32)
+    _need(C, "C", torch.float32, like=X)
     B, N, D = _shape3(X)
-    K = C.shape[-2]
+    K = _rows(C, "C", B, D)
     dt = _dtype(X)
-    labels = torch.empty(X.shape[:-1], dtype=torch.int32, device=X.device) if labels is None else labels
-    ws = _workspace(N, D, K, B, dt, X.device, ws)
+    if labels is None:
+        labels = torch.empty(X.shape[:-1], dtype=torch.int32, device=X.device)
+    else:
+        _need(labels, "labels", torch.int32, like=X)
+        _count(labels, "labels", B * N)
+    ws, ws_bytes = _workspace(N, D, K, B, dt, X.device, ws)
     pb, waves, ms = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_float(0.0)
-    _check(_lib.kmeans_tune(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(labels), _ptr(ws), ws.numel(), _stream(stream),
+    _check(_lib.kmeans_tune(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(labels), _ptr(ws), ws_bytes, _stream(stream),
                             ctypes.byref(pb), ctypes.byref(waves), ctypes.byref(ms)))
     return pb.value, waves.value, ms.value
 
@@ -296,6 +354,7 @@ def tune_load(path: str):
     _check(_lib.kmeans_tune_load(os.fsencode(path)))
 
 
+@_on_tensor_device
 def fit_streamed(X_host, C0, iters: int, device_x_budget: int, *, history: bool = False, stream=None):
     """Out-of-core Lloyd iteration over a pinned host tensor X_host [N, D].
 
@@ -306,7 +365,7 @@ def fit_streamed(X_host, C0, iters: int, device_x_budget: int, *, history: bool 
         raise KMeansError(KM_EINVAL, "X_host must be a contiguous [N, D] tensor")
     _need(C0, "C0", torch.float32)
     N, D = X_host.shape
-    K = C0.shape[-2]
+    K = _rows(C0, "C0", 1, D)
     dt = _dtype(X_host)
     labels = torch.empty(N, dtype=torch.int32, pin_memory=True)
     C = torch.empty_like(C0)

@@ -260,6 +260,34 @@ def test_wide_digit_update(km, n, k, batch):
     H.log(f"wide-digit update n={n} k={k} B={batch}: worst centroid err {worst:.2e}")
 
 
+def test_binding_rejects_mismatched_arguments(km):
+    """The Python binding checks shapes, devices and caller buffers before any
+    launch: a mismatch raises KMeansError instead of reaching a kernel."""
+    X = torch.zeros(2, 100, 32, dtype=torch.float16, device="cuda")
+    C = torch.zeros(2, 10, 32, dtype=torch.float32, device="cuda")
+    lab = torch.zeros(2, 100, dtype=torch.int32, device="cuda")
+    bad = [
+        lambda: km.assign(X, torch.zeros(2, 10, 16, device="cuda")),                 # D differs
+        lambda: km.assign(X, torch.zeros(3, 10, 32, device="cuda")),                 # B differs
+        lambda: km.assign(X, C, labels=torch.zeros(2, 99, dtype=torch.int32, device="cuda")),
+        lambda: km.update(X, lab[:, :50].contiguous(), C),                           # labels too short
+        lambda: km.update(X, lab, C, C_new=torch.zeros(2, 9, 32, device="cuda")),    # C_new too small
+        lambda: km.assign(X, C, ws=torch.zeros(1 << 20, dtype=torch.uint8)),         # workspace on the host
+        lambda: km.assign(X, C, ws=torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")[::2]),  # strided
+        lambda: km.assign_soft(X, C, 1.0, log_w=torch.zeros(2, 9, device="cuda")),
+        lambda: km.gauss_sum(X, C, torch.zeros(2, 9, device="cuda"), 1.0),
+        lambda: km.fit(X, torch.zeros(10, 32, device="cuda"), 2),                    # [K, D] with B = 2
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(km.KMeansError):
+            call()
+    # the good call still works, with a caller workspace of another dtype
+    ws = torch.empty(km.workspace_bytes(100, 32, 10, 2, torch.float16) // 4 + 1, dtype=torch.float32, device="cuda")
+    labels, _, J = km.assign(X, C, ws=ws)
+    torch.cuda.synchronize()
+    assert labels.shape == (2, 100) and torch.all(J == 0)
+
+
 def test_determinism_and_resume(km):
     p = datagen.make("c3", n=50000, k=777, seed=6)
     X, C0 = p.X.cuda(), p.C0.cuda()
