@@ -168,7 +168,14 @@ __device__ __forceinline__ void improve(const f32x16& acc, float tmax, float& be
 //            labels = the nearest source.
 enum AssignMode : int { kArgmax = 0, kTop2 = 1, kSoft = 2, kGauss = 3 };
 
-template <class T, int D, int PB, int W, int MODE>
+// RES (argmax, one point block, 8 waves, all K centroids in one tile): a
+// workgroup takes a contiguous run of jobs, so consecutive jobs share an
+// instance and its centroid tile stays in LDS; the second tile buffer then
+// stages points instead: each wave copies its next job's 32 rows there
+// (global->LDS, XOR-swizzled like the tile) while it computes the current
+// job, so a job starts from LDS instead of waiting on HBM.  Products, their
+// order and the epilogue are those of the plain (1, 8) configuration.
+template <class T, int D, int PB, int W, int MODE, bool RES = false>
 __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* __restrict__ X,
                                                         const typename T::raw* __restrict__ Ch,
                                                         const float* __restrict__ hb, int64_t N, int K, int B,
@@ -184,6 +191,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
   __shared__ __align__(16) float tb[2][TK];  // read back as float4
   __shared__ __align__(16) float tw[MODE == kGauss ? 2 : 1][MODE == kGauss ? TK : 4];  // kGauss: weights
   __shared__ double wsum[W];
+  static_assert(!RES || (MODE == kArgmax && PB == 1 && TK == Cfg::ROWS), "resident tile: one tile, rows = tile rows");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -193,8 +201,39 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
 
   // Persistent loop over (instance, point block).  Every workgroup does the
   // same amount of work per block, so the workgroups resident on an XCD sweep
-  // the centroids in step and share each tile through that XCD's L2.
-  for (int64_t job = blockIdx.x; job < nblk * B; job += gridDim.x) {
+  // the centroids in step and share each tile through that XCD's L2.  (RES:
+  // a contiguous, balanced run of jobs per workgroup.)
+  int64_t jbeg = blockIdx.x, jend = nblk * B, jstep = gridDim.x;
+  if constexpr (RES) {
+    const int64_t nj = nblk * B, q = nj / gridDim.x, r = nj % gridDim.x, g = blockIdx.x;
+    jbeg = g * q + (g < r ? g : r);
+    jend = jbeg + q + (g < r ? 1 : 0);
+    jstep = 1;
+  }
+  // RES: wave w's 32 rows of job j go to rows [32 w, 32 w + 32) of tile[1],
+  // chunk c of row m at chunk (c ^ (m % NCH)) of that row; lane l of the
+  // instruction i writes chunk 64 i + l of the wave's slice.
+  auto stage_points = [&](int64_t j) {
+    const int bj = (int)(j / nblk);
+    const int64_t pj = (j - (int64_t)bj * nblk) * Cfg::ROWS + (int64_t)w * 32;
+    const typename T::raw* Xj = X + (int64_t)bj * N * D;
+#pragma unroll
+    for (int i = 0; i < 32 * NCH / 64; ++i) {
+      const int qc = i * 64 + lane;
+      const int lr = qc / NCH, pc = qc % NCH;
+      const int m = w * 32 + lr;
+      int64_t n = pj + lr;
+      n = n < N ? n : N - 1;
+      const uint4* src = reinterpret_cast<const uint4*>(Xj + n * D) + (pc ^ (m & (NCH - 1)));
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&tile[1][w * 32 * NCH + i * 64],
+                                       16, 0, 0);
+    }
+  };
+  int cur_b = -1;
+  if constexpr (RES) {
+    if (jbeg < jend) stage_points(jbeg);
+  }
+  for (int64_t job = jbeg; job < jend; job += jstep) {
     const int b = (int)(job / nblk);
     const int64_t blk = job - (int64_t)b * nblk;
     const typename T::raw* Xb = X + (int64_t)b * N * D;
@@ -202,16 +241,6 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
     const float* hbb = hb + (int64_t)b * kpad(K);
     const int64_t p0 = blk * Cfg::ROWS + (int64_t)w * (PB * 32);
 
-    // point fragments: lane half h holds dims [h*D/2, (h+1)*D/2) of point col
-    uint4 xf[PB][HV];
-#pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      int64_t n = p0 + p * 32 + col;
-      n = n < N ? n : N - 1;
-      const uint4* src = reinterpret_cast<const uint4*>(Xb + n * D) + h * HV;
-#pragma unroll
-      for (int v = 0; v < HV; ++v) xf[p][v] = src[v];
-    }
 
     // Tile t goes straight from global memory into LDS buffer `buf`
     // (global_load_lds: lane l of a wave writes 16 bytes at the instruction's
@@ -263,9 +292,40 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
       lsum[p] = 0.f;
     }
 
-    issue_tile(0, 0);
-    wait_tile();
-    __syncthreads();
+    // point fragments: lane half h holds dims [h*D/2, (h+1)*D/2) of point col
+    uint4 xf[PB][HV];
+    if constexpr (RES) {
+      // a new instance: every wave is done with the old tile, then load it
+      const bool fresh = b != cur_b;
+      if (fresh) {
+        __syncthreads();
+        issue_tile(0, 0);
+        cur_b = b;
+      }
+      wait_tile();  // this wave's staged points (and the tile it copied) have landed
+      if (fresh) __syncthreads();
+      const int m = w * 32 + col;
+#pragma unroll
+      for (int v = 0; v < HV; ++v) {
+        const int c = h * HV + v;
+        xf[0][v] = tile[1][m * NCH + (c ^ (m & (NCH - 1)))];
+      }
+      // the reads above complete before the next job's rows overwrite the slice
+      __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */
+      if (job + 1 < jend) stage_points(job + 1);
+    } else {
+#pragma unroll
+      for (int p = 0; p < PB; ++p) {
+        int64_t n = p0 + p * 32 + col;
+        n = n < N ? n : N - 1;
+        const uint4* src = reinterpret_cast<const uint4*>(Xb + n * D) + h * HV;
+#pragma unroll
+        for (int v = 0; v < HV; ++v) xf[p][v] = src[v];
+      }
+      issue_tile(0, 0);
+      wait_tile();
+      __syncthreads();
+    }
 
     // The centroid tile is consumed in groups of G sub-blocks of 32
     // centroids: the G x PB accumulation chains of a group are issued
@@ -427,8 +487,10 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
           reduce_group(acc, base, wv);
         }
       }
-      wait_tile();
-      __syncthreads();
+      if constexpr (!RES) {  // (RES: the single tile stays; the staged rows are waited for at the next job)
+        wait_tile();
+        __syncthreads();
+      }
     }
     if constexpr (DELAY) reduce_group(prev, prev_base, wprev);
 
@@ -564,7 +626,7 @@ hipError_t prep_t(const float* C, void* Chat, float* hb, int64_t B, int K, const
 
 // Workgroup slots of the persistent grid on the current device: as many
 // workgroups as fit at once (queried once per thread and device).
-template <class T, int D, int PB, int W, int MODE>
+template <class T, int D, int PB, int W, int MODE, bool RES = false>
 hipError_t assign_slots(int* slots) {
   using Cfg = AssignCfg<T, D, PB, W>;
   static thread_local int cached_dev = -1, cached_slots = 0;
@@ -574,8 +636,8 @@ hipError_t assign_slots(int* slots) {
   if (dev != cached_dev) {
     int cus = 0, per_cu = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, assign_kernel<T, D, PB, W, MODE>, Cfg::THREADS,
-                                                          0)) != hipSuccess)
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, assign_kernel<T, D, PB, W, MODE, RES>,
+                                                          Cfg::THREADS, 0)) != hipSuccess)
       return e;
     cached_slots = cus * (per_cu > 0 ? per_cu : 1);
     cached_dev = dev;
@@ -584,16 +646,16 @@ hipError_t assign_slots(int* slots) {
   return hipSuccess;
 }
 
-template <class T, int D, int PB, int W, int MODE>
+template <class T, int D, int PB, int W, int MODE, bool RES = false>
 hipError_t assign_t(const void* X, const void* Chat, const float* hb, int64_t N, int K, int B, int32_t* labels,
                     float* min_d2, double* part, SoftArgs soft, hipStream_t s) {
   using Cfg = AssignCfg<T, D, PB, W>;
   const int64_t jobs = (N + Cfg::ROWS - 1) / Cfg::ROWS * (int64_t)B;
   int slots = 0;
-  const hipError_t e = assign_slots<T, D, PB, W, MODE>(&slots);
+  const hipError_t e = assign_slots<T, D, PB, W, MODE, RES>(&slots);
   if (e != hipSuccess) return e;
   const int64_t grid = jobs < slots ? jobs : slots;
-  assign_kernel<T, D, PB, W, MODE><<<dim3((unsigned)grid), dim3(Cfg::THREADS), 0, s>>>(
+  assign_kernel<T, D, PB, W, MODE, RES><<<dim3((unsigned)grid), dim3(Cfg::THREADS), 0, s>>>(
       reinterpret_cast<const typename T::raw*>(X), reinterpret_cast<const typename T::raw*>(Chat), hb, N, K, B,
       labels, min_d2, part, soft);
   return hipGetLastError();
@@ -625,6 +687,12 @@ hipError_t assign_cfg(AssignConfig c, const void* X, const void* Chat, const flo
                       int32_t* labels, float* min_d2, double* part, SoftArgs soft, hipStream_t s) {
   constexpr int rb = D * T::SZ;
   if constexpr (MODE == kArgmax) {
+    // one point block, 8 waves, all centroids in one 256-row tile: the
+    // resident-tile form of that configuration
+    if constexpr (rb <= 256) {
+      if (c.pb == 1 && c.waves == 8 && K <= AssignCfg<T, D, 1, 8>::TK)
+        return assign_t<T, D, 1, 8, MODE, true>(X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
+    }
 #define FKM_CASE(PB_, W_)                                                                      \
     if constexpr (cfg_compiled(T::SZ, rb, PB_, W_)) {                                          \
       if (c.pb == PB_ && c.waves == W_)                                                        \
@@ -649,6 +717,12 @@ template <class T, int D>
 hipError_t assign_prime_cfg(AssignConfig c) {
   constexpr int rb = D * T::SZ;
   int slots = 0;
+  if constexpr (rb <= 256) {  // (1, 8) may launch its resident-tile form: query that too
+    if (c.pb == 1 && c.waves == 8) {
+      const hipError_t e = assign_slots<T, D, 1, 8, kArgmax, true>(&slots);
+      if (e != hipSuccess) return e;
+    }
+  }
 #define FKM_CASE(PB_, W_)                                              \
   if constexpr (cfg_compiled(T::SZ, rb, PB_, W_)) {                    \
     if (c.pb == PB_ && c.waves == W_) return assign_slots<T, D, PB_, W_, kArgmax>(&slots); \
@@ -751,6 +825,12 @@ AssignConfig assign_pick(int dt, int D, int64_t N, int B, int K) {
   // overheads and the uneven last round lose more.
   const bool long_sweep = K >= 8192 && (N + 767) / 768 * (int64_t)B >= 4096;
   if (long_sweep && cfg_compiled(sz, rb, 3, 8)) return AssignConfig{3, 8};
+  // All centroids in one tile (rows of at most 256 bytes, K <= 256) and at
+  // least 2048 jobs of 256 points: the resident-tile form of (1, 8) keeps
+  // each instance's tile in LDS and stages the next job's points while the
+  // current one computes (measured: 5.6% more fit iterations at 64 instances
+  // of 16,384 points, K = 256; no change at 2^16 points, K = 64).
+  if (rb <= 256 && K <= 256 && (N + 255) / 256 * (int64_t)B >= 2048) return AssignConfig{1, 8};
   const AssignConfig order[] = {{2, 8}, {1, 8}, {1, 4}};
   for (const AssignConfig& c : order) {
     if (!cfg_compiled(sz, rb, c.pb, c.waves)) continue;

@@ -460,6 +460,34 @@ def test_tune_and_every_config_agree(km, dtype, d, tmp_path):
     H.check_assign(Xd, C.cpu().numpy(), ref[0].numpy(), ref[2], dtype, min_d2=ref[1].numpy(), tag=f"tune-{dtype}-{d}")
 
 
+def test_resident_tile_batched_agrees(km, tmp_path):
+    """The resident-tile form of (1 block, 8 waves), taken when all K
+    centroids fit one tile: a workgroup's contiguous run of jobs crosses
+    instance boundaries here (3 instances of 100,003 points, about 4.6 jobs
+    per workgroup), so the tile is reloaded inside the run.  Labels and
+    distances equal the other configurations bit for bit, and the oracle."""
+    n, d, k, batch = 100_003, 64, 200, 3
+    X, C0, _, _ = datagen.mixture(n, d, 40, dtype="bf16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                  weights=None, workload_code=64, seed=1, k=k, batch=batch)
+    X, C = X.cuda(), C0.cuda()
+    ref = None
+    for c in [(1, 8), (1, 4), (2, 8)]:
+        f = tmp_path / f"r{c[0]}_{c[1]}.txt"
+        f.write_text(f"2 {d} {n} {batch} {k} {c[0]} {c[1]}\n")
+        km.tune_load(str(f))
+        lab, md, J = km.assign(X, C, want_min_d2=True)
+        torch.cuda.synchronize()
+        got = (lab.cpu(), md.cpu(), J.cpu())
+        if ref is None:
+            ref = got
+        else:
+            assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), f"config {c} differs"
+            assert torch.allclose(got[2], ref[2], rtol=1e-12, atol=0.0), f"config {c}: inertia differs"
+    for b in range(batch):
+        H.check_assign(H.decode(X[b].cpu(), "bf16"), C[b].cpu().numpy(), ref[0][b].numpy(), float(ref[2][b]), "bf16",
+                       min_d2=ref[1][b].numpy(), tag=f"resident b={b}")
+
+
 def _mixture(n, d, k, dtype, seed, batch=1, m=None):
     return datagen.mixture(n, d, m or max(2, k // 2), dtype=dtype, center_dist="normal", center_scale=2.0,
                            sigma=1.0, weights=None, workload_code=59, seed=seed, batch=batch, k=k)
