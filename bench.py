@@ -153,7 +153,7 @@ def probe(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on exactly one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     import torch
