@@ -488,6 +488,27 @@ def test_resident_tile_batched_agrees(km, tmp_path):
                        min_d2=ref[1][b].numpy(), tag=f"resident b={b}")
 
 
+def test_fit_with_resident_tile_equals_stepwise(km, tmp_path):
+    """A fit whose assignment runs the resident-tile form (forced through the
+    tuning table for this shape): the captured and replayed fit equals the
+    same iterations as stand-alone calls bit for bit."""
+    n, d, k, batch, iters = 20_011, 64, 100, 3, 3
+    X, C0, _, _ = datagen.mixture(n, d, 30, dtype="fp16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                  weights=None, workload_code=65, seed=2, k=k, batch=batch)
+    f = tmp_path / "resident.txt"
+    f.write_text(f"1 {d} {n} {batch} {k} 1 8\n")
+    km.tune_load(str(f))
+    Xc, C = X.cuda(), C0.cuda()
+    Cs = C.clone()
+    for t in range(iters):
+        lab, _, J = km.assign(Xc, Cs)
+        Cs, _ = km.update(Xc, lab, Cs)
+    for rep in range(2):  # capture, then replay
+        lab_f, C_f, J_f, _ = km.fit(Xc, C, iters, history=True)
+        torch.cuda.synchronize()
+        assert torch.equal(lab, lab_f) and torch.equal(Cs, C_f) and torch.equal(J, J_f), f"replay {rep} differs"
+
+
 def _mixture(n, d, k, dtype, seed, batch=1, m=None):
     return datagen.mixture(n, d, m or max(2, k // 2), dtype=dtype, center_dist="normal", center_scale=2.0,
                            sigma=1.0, weights=None, workload_code=59, seed=seed, batch=batch, k=k)
