@@ -64,12 +64,8 @@ def cpu_baseline(p, sample_rows):
     sample of the same workload, scaled linearly to the full N."""
     import oracle
     from tests.gpu_harness import decode
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        cores = int(blas[0]["num_threads"]) if blas else 1
-    except Exception:  # pragma: no cover
-        cores = 1
+    host = host_info()
+    cores = host["blas"]["threads"] or 1
     B = p.B
     rows = min(sample_rows, p.N)
     Xs = p.X[0, :rows]
@@ -85,7 +81,35 @@ def cpu_baseline(p, sample_rows):
     return {"value": 1.0 / sec_per_iter, "unit": "iter/s", "cores": cores, "kind": "oracle",
             "sample": (f"one oracle Lloyd iteration (fp64 assign + update) on the first {rows:,} of "
                        f"{p.N:,} rows x {B} instance(s), all K={p.K:,} centroids, {dt:.1f} s, scaled "
-                       f"linearly by N/{rows:,}")}
+                       f"linearly by N/{rows:,}; cores = the BLAS threads (the oracle's matrix products; its "
+                       f"other numpy steps run on one thread)"),
+            "cpu_count": host["cpu_count"], "cpu_model": host["cpu_model"], "blas": host["blas"]}
+
+
+def host_info():
+    """The host the oracle runs on: logical CPUs, the CPU model from
+    /proc/cpuinfo, and numpy's BLAS (vendor, version, threads) as
+    threadpoolctl reports it."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = {"vendor": None, "version": None, "threads": None}
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = {"vendor": i.get("internal_api"), "version": i.get("version"),
+                        "threads": int(i.get("num_threads") or 0) or None}
+                break
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_count": os.cpu_count(), "cpu_model": model, "blas": blas}
 
 
 ASSIGN_SOURCES = ["exact_means_clustering_amd/csrc/assign.hip", "exact_means_clustering_amd/csrc/common.h"]

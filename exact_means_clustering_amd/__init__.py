@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "assign_top2", "assign_soft", "gauss_sum", "seed", "update",
-           "fit", "fit_streamed", "tune", "tune_save", "tune_load", "DTYPES"]
+           "fit", "fit_streamed", "tune", "tune_save", "tune_load", "assign_configs", "DTYPES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libflashkm.so"
@@ -68,6 +68,8 @@ def _load(path=None):
     lib.kmeans_tune.restype = ctypes.c_int
     lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
     lib.kmeans_tune_save.restype = ctypes.c_int
+    lib.kmeans_assign_configs.argtypes = [i32, i32, P, P, i32, P]
+    lib.kmeans_assign_configs.restype = ctypes.c_int
     lib.kmeans_tune_load.argtypes = [ctypes.c_char_p]
     lib.kmeans_tune_load.restype = ctypes.c_int
     lib.kmeans_last_error.argtypes = []
@@ -347,6 +349,16 @@ def tune(X, C, *, labels=None, ws=None, stream=None):
 def tune_save(path: str):
     """Write the tuning table as text ("dtype D N B K pb waves" per line)."""
     _check(_lib.kmeans_tune_save(os.fsencode(path)))
+
+
+def assign_configs(dtype, D: int) -> list:
+    """The (pb, waves) assignment configurations compiled for rows of D elements of dtype."""
+    dt = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    pb, waves, n = (ctypes.c_int32 * 8)(), (ctypes.c_int32 * 8)(), ctypes.c_int32(0)
+    _check(_lib.kmeans_assign_configs(dt, int(D), pb, waves, 8, ctypes.byref(n)))
+    if n.value > 8:
+        raise KMeansError(KM_EINVAL, f"{n.value} configurations; the binding reads at most 8")
+    return [(pb[i], waves[i]) for i in range(n.value)]
 
 
 def tune_load(path: str):

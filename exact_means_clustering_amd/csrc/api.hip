@@ -88,7 +88,13 @@ struct FitArgs {
   void* ws;
   size_t ws_bytes;
   int dev;
-  auto tie() const { return std::tie(X, dt, N, D, B, C0, K, iters, labels, C_out, inertia, hist, ws, ws_bytes, dev); }
+  // the assign configuration chosen for the shape when the call was made:
+  // part of the key, so a replay never runs a configuration the tuning table
+  // or the environment no longer selects
+  AssignConfig cfg;
+  auto tie() const {
+    return std::tie(X, dt, N, D, B, C0, K, iters, labels, C_out, inertia, hist, ws, ws_bytes, dev, cfg.pb, cfg.waves);
+  }
   bool operator==(const FitArgs& o) const { return tie() == o.tie(); }
 };
 
@@ -100,7 +106,7 @@ struct FitArgs {
 int enqueue_fit(const FitArgs& a, Work& w, hipStream_t s) {
   const int64_t n = a.N * a.B;
   const uint32_t nseg = (uint32_t)((int64_t)a.B * a.K);
-  const AssignConfig cfg = assign_pick(a.dt, a.D, a.N, a.B, a.K);
+  const AssignConfig cfg = a.cfg;
   const int64_t nwg = (a.N + cfg.rows() - 1) / cfg.rows();
   KM_HIP(launch_prep(a.dt, a.D, a.C0, w.chat, w.hb, a.B, a.K, s), "centroid prep launch");
   for (int t = 0; t < a.iters; ++t) {
@@ -160,7 +166,7 @@ int fit_graph(const FitArgs& a, Work& w, hipStream_t s) {
       return KM_OK;
     }
   // device queries the launches need happen now, not during the capture
-  KM_HIP(assign_prime(a.dt, a.D, assign_pick(a.dt, a.D, a.N, a.B, a.K)), "assign configuration query");
+  KM_HIP(assign_prime(a.dt, a.D, a.cfg), "assign configuration query");
   static hipStream_t capture[64] = {};
   if (a.dev < 0 || a.dev >= 64) return fail(KM_EINVAL, "device index %d out of range", a.dev);
   if (!capture[a.dev]) KM_HIP(hipStreamCreateWithFlags(&capture[a.dev], hipStreamNonBlocking), "stream create");
@@ -372,7 +378,9 @@ int kmeans_fit(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, co
   hipStream_t s = (hipStream_t)stream;
   int dev = 0;
   KM_HIP(hipGetDevice(&dev), "device query");
-  const FitArgs a{X, dtype, N, D, B, C0, K, iters, labels, C_out, inertia, inertia_hist, ws, ws_bytes, dev};
+  const FitArgs a{X,     dtype,   N,            D,  B,        C0,  K,
+                  iters, labels,  C_out,        inertia,      inertia_hist, ws,  ws_bytes,
+                  dev,   assign_pick(dtype, D, N, B, K)};
   return graphs_enabled() ? fit_graph(a, w, s) : enqueue_fit(a, w, s);
 }
 

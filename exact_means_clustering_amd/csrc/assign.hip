@@ -190,7 +190,11 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
   __shared__ uint4 tile[2][Cfg::TILE_CH];
   __shared__ __align__(16) float tb[2][TK];  // read back as float4
   __shared__ __align__(16) float tw[MODE == kGauss ? 2 : 1][MODE == kGauss ? TK : 4];  // kGauss: weights
-  __shared__ double wsum[W];
+  // per-wave inertia partials, double-buffered by job parity: in the RES form
+  // consecutive jobs need not pass a workgroup barrier between one job's read
+  // of the partials (thread 0) and the next job's writes (every wave); the
+  // barrier of the job in between orders the reuse of a buffer
+  __shared__ double wsum[2][W];
   static_assert(!RES || (MODE == kArgmax && PB == 1 && TK == Cfg::ROWS), "resident tile: one tile, rows = tile rows");
 
   const int tid = threadIdx.x;
@@ -233,7 +237,8 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
   if constexpr (RES) {
     if (jbeg < jend) stage_points(jbeg);
   }
-  for (int64_t job = jbeg; job < jend; job += jstep) {
+  int par = 0;  // parity of this workgroup's job count (selects the wsum buffer)
+  for (int64_t job = jbeg; job < jend; job += jstep, par ^= 1) {
     const int b = (int)(job / nblk);
     const int64_t blk = job - (int64_t)b * nblk;
     const typename T::raw* Xb = X + (int64_t)b * N * D;
@@ -500,8 +505,9 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
     // (row k, chunks swizzled as the tile was written), so the row is read
     // there instead of from global memory.  The workgroup barrier after the
     // distances (the per-workgroup sum) keeps the next job's tile load from
-    // overwriting the buffer first; kTop2 has no such barrier and reads
-    // global memory.
+    // overwriting the buffer first (RES reloads the tile only for a new
+    // instance, behind a barrier of its own); kTop2 has no such barrier and
+    // reads global memory.
     auto direct_d2 = [&](int p, int k) -> float {
       const uint4* cr = reinterpret_cast<const uint4*>(Cb + (int64_t)k * D) + h * HV;
       const bool in_lds = MODE != kTop2 && ntiles == 1;
@@ -590,12 +596,12 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
     }
     if constexpr (MODE != kTop2) {
       wacc = wave_sum_f64(wacc);
-      if (lane == 0) wsum[w] = wacc;
+      if (lane == 0) wsum[par][w] = wacc;
       __syncthreads();
       if (tid == 0) {
         double tot = 0.0;
 #pragma unroll
-        for (int i = 0; i < W; ++i) tot += wsum[i];
+        for (int i = 0; i < W; ++i) tot += wsum[par][i];
         part[(int64_t)b * nblk + blk] = tot;
       }
     }
@@ -689,7 +695,7 @@ hipError_t assign_cfg(AssignConfig c, const void* X, const void* Chat, const flo
   if constexpr (MODE == kArgmax) {
     // one point block, 8 waves, all centroids in one 256-row tile: the
     // resident-tile form of that configuration
-    if constexpr (rb <= 256) {
+    if constexpr (rb <= 256 && AssignCfg<T, D, 1, 8>::TK == AssignCfg<T, D, 1, 8>::ROWS) {
       if (c.pb == 1 && c.waves == 8 && K <= AssignCfg<T, D, 1, 8>::TK)
         return assign_t<T, D, 1, 8, MODE, true>(X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
     }
@@ -717,7 +723,8 @@ template <class T, int D>
 hipError_t assign_prime_cfg(AssignConfig c) {
   constexpr int rb = D * T::SZ;
   int slots = 0;
-  if constexpr (rb <= 256) {  // (1, 8) may launch its resident-tile form: query that too
+  // (1, 8) may launch its resident-tile form: query that too
+  if constexpr (rb <= 256 && AssignCfg<T, D, 1, 8>::TK == AssignCfg<T, D, 1, 8>::ROWS) {
     if (c.pb == 1 && c.waves == 8) {
       const hipError_t e = assign_slots<T, D, 1, 8, kArgmax, true>(&slots);
       if (e != hipSuccess) return e;

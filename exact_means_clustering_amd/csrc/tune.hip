@@ -149,6 +149,21 @@ int kmeans_tune_save(const char* path) {
   return KM_OK;
 }
 
+int kmeans_assign_configs(int32_t dtype, int32_t D, int32_t* pb, int32_t* waves, int32_t cap, int32_t* count) {
+  err_buf()[0] = 0;
+  if (!count || cap < 0 || (cap > 0 && (!pb || !waves)))
+    return fail(KM_EINVAL, "count must be non-null, and pb and waves hold cap >= 0 entries");
+  if (!valid_shape(dtype, D, 1, 1, 1)) return fail(KM_EUNSUPPORTED, "unsupported dtype %d or D=%d", dtype, D);
+  AssignConfig all[8];
+  const int n = assign_configs(dtype, D, all, 8);
+  for (int i = 0; i < n && i < cap; ++i) {
+    pb[i] = all[i].pb;
+    waves[i] = all[i].waves;
+  }
+  *count = n;
+  return KM_OK;
+}
+
 int kmeans_tune_load(const char* path) {
   err_buf()[0] = 0;
   if (!path) return fail(KM_EINVAL, "path is null");

@@ -113,11 +113,13 @@ KM_API int kmeans_update(const void* X, int32_t dtype, int64_t N, int32_t D, int
  * Every round equals one kmeans_assign followed by one kmeans_update bit for
  * bit (internally the inertia sum and the next round's centroid preparation
  * ride along with the update's kernels).
- * The first call with a given argument list (pointers, sizes, iters, device)
- * captures the whole fit into a HIP graph; later calls with the same list
- * replay it with one graph launch (the last 8 lists are kept; the buffers'
- * contents may change between calls).  Results are identical to direct
- * launches, which the environment variable FLASHKM_FIT_GRAPH=0 selects. */
+ * The first call with a given argument list (pointers, sizes, iters, device,
+ * and the assignment tile configuration chosen for the shape at the time of
+ * the call, see kmeans_tune) captures the whole fit into a HIP graph; later
+ * calls with the same list replay it with one graph launch (the last 8 lists
+ * are kept; the buffers' contents may change between calls).  Results are
+ * identical to direct launches, which the environment variable
+ * FLASHKM_FIT_GRAPH=0 selects. */
 KM_API int kmeans_fit(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
                const float* C0, int32_t K, int32_t iters,
                int32_t* labels, float* C_out, double* inertia, double* inertia_hist,
@@ -239,6 +241,13 @@ KM_API int kmeans_tune(const void* X, int32_t dtype, int64_t N, int32_t D, int32
                        void* ws, size_t ws_bytes, void* stream,
                        int32_t* pb, int32_t* waves, float* ms);
 KM_API int kmeans_tune_save(const char* path);
+/* The configurations compiled for rows of D elements of `dtype`, the set
+ * kmeans_tune chooses from and a tuning-table line may name: the first
+ * min(cap, *count) pairs go to pb[i], waves[i] (host arrays, nullable when
+ * cap = 0) and *count receives their number.  KM_EUNSUPPORTED for a dtype or
+ * D the library does not support.  Does not touch the GPU. */
+KM_API int kmeans_assign_configs(int32_t dtype, int32_t D, int32_t* pb, int32_t* waves, int32_t cap,
+                                 int32_t* count);
 KM_API int kmeans_tune_load(const char* path);
 
 /* Text of the last error set on the calling thread ("" if none). */

@@ -100,6 +100,34 @@ def check_update(Xd, labels_gpu, C_prev_gpu, C_new_gpu, counts_gpu, K, tag=""):
     return err
 
 
+def check_step(km, X, Xd, C, fmt, *, sample=None, rng=None, tag=""):
+    """One teacher-forced iteration from the GPU state C [B,K,D] (device):
+    GPU assign + update, then the oracle's assign with C (labels on every row,
+    or on `sample` seeded rows per instance plus the full-row inertia
+    property) and the oracle's update from the GPU labels on every row.
+    Returns (labels, C_new, inertia, near-tie count, centroid error)."""
+    B, N, _ = X.shape
+    K = C.shape[1]
+    labels, md, inertia = km.assign(X, C, want_min_d2=True)
+    C_new, counts = km.update(X, labels, C)
+    torch.cuda.synchronize()
+    lab_c, md_c, J_c = labels.cpu().numpy(), md.cpu().numpy(), inertia.cpu().numpy()
+    Cc, Cn_c, cnt_c = C.cpu().numpy(), C_new.cpu().numpy(), counts.cpu().numpy()
+    ties, cerr = 0, 0.0
+    for b in range(B):
+        rows = None
+        if sample is not None and N > sample:
+            rows = np.sort((rng or np.random.default_rng(0)).choice(N, size=sample, replace=False))
+        rep = check_assign(Xd[b], Cc[b], lab_c[b], J_c[b], fmt, min_d2=md_c[b], rows=rows, tag=f"{tag} b{b}")
+        if rows is not None:
+            check_inertia_of_labels(Xd[b], Cc[b], lab_c[b], J_c[b], fmt, tag=f"{tag} b{b}")
+        ties += rep["excused"]
+        cerr = max(cerr, check_update(Xd[b], lab_c[b], Cc[b], Cn_c[b], cnt_c[b], K, tag=f"{tag} b{b}"))
+    log(f"{tag}: ok ({'all' if sample is None or N <= sample else sample} label rows per instance, "
+        f"near-ties excused {ties}, centroid err {cerr:.2e})")
+    return labels, C_new, inertia, ties, cerr
+
+
 def teacher_forced(km, X_cpu, C0_cpu, iters, *, sample=None, tag="", check_fit=True, seed=0):
     """Run `iters` GPU iterations step by step and check each one against the
     oracle.  X_cpu [B,N,D], C0_cpu [B,K,D].  Returns per-iteration stats."""

@@ -29,8 +29,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {
         "kmeans_workspace_bytes", "kmeans_assign", "kmeans_update", "kmeans_fit", "kmeans_fit_streamed",
-        "kmeans_assign_top2", "kmeans_assign_soft", "kmeans_gauss_sum", "kmeans_seed", "kmeans_tune", "kmeans_tune_save", "kmeans_tune_load",
-        "kmeans_last_error"}
+        "kmeans_assign_top2", "kmeans_assign_soft", "kmeans_gauss_sum", "kmeans_seed", "kmeans_tune", "kmeans_tune_save",
+        "kmeans_tune_load", "kmeans_assign_configs", "kmeans_last_error"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -53,8 +53,36 @@ def _sig(lib):
     lib.kmeans_seed.argtypes = [P, i32, i64, i32, i32, i32, i32, P, P, P, P, P, sz, P]
     lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
     lib.kmeans_tune_load.argtypes = [ctypes.c_char_p]
+    lib.kmeans_assign_configs.argtypes = [i32, i32, P, P, i32, P]
     lib.kmeans_last_error.restype = ctypes.c_char_p
     return lib
+
+
+def test_assign_configs_query(lib):
+    """The compiled configurations per row size: (1, 4) everywhere; deeper
+    blocking only where the point fragments fit the registers (rows of at most
+    256 bytes for (2, 8), (4, 4) and the 16-bit (3, 8); 128 bytes for fp32 at
+    (3, 8); 512 bytes for (2, 4) and (1, 8))."""
+    lib = _sig(lib)
+
+    def q(dt, d):
+        pb, w, n = (ctypes.c_int32 * 8)(), (ctypes.c_int32 * 8)(), ctypes.c_int32(-1)
+        assert lib.kmeans_assign_configs(dt, d, pb, w, 8, ctypes.byref(n)) == 0
+        return {(pb[i], w[i]) for i in range(n.value)}
+
+    every = {(4, 4), (3, 8), (2, 8), (2, 4), (1, 8), (1, 4)}
+    assert q(2, 128) == every                      # bf16, 256-byte rows
+    assert q(1, 64) == every                       # fp16, 128-byte rows
+    assert q(0, 32) == every                       # fp32, 128-byte rows
+    assert q(0, 64) == every - {(3, 8)}            # fp32, 256-byte rows
+    assert q(1, 256) == {(2, 4), (1, 8), (1, 4)}   # 512-byte rows
+    assert q(0, 256) == {(1, 4)}                   # 1 KB rows
+    n = ctypes.c_int32(-1)
+    assert lib.kmeans_assign_configs(2, 128, None, None, 0, ctypes.byref(n)) == 0 and n.value == 6
+    assert lib.kmeans_assign_configs(2, 100, None, None, 0, ctypes.byref(n)) == 2     # unsupported D
+    assert lib.kmeans_assign_configs(9, 128, None, None, 0, ctypes.byref(n)) == 2     # bad dtype
+    assert lib.kmeans_assign_configs(2, 128, None, None, 4, ctypes.byref(n)) == 1     # cap > 0, null arrays
+    assert lib.kmeans_assign_configs(2, 128, None, None, 0, None) == 1                # null count
 
 
 def test_workspace_bytes(lib):

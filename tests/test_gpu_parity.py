@@ -336,9 +336,42 @@ def test_streamed_matches_in_core(km):
     assert oracle.centroid_rel_err(C_s.cpu().numpy(), C_i.cpu().numpy(), rms) <= 1e-4
     mism = int((lab_s != lab_i.cpu()).sum())
     assert mism <= 1e-4 * X.shape[0], mism
-    # teacher-forced: the streamed update from its own labels matches the oracle
-    _, C_prev, _, _ = km.fit_streamed(Xp, p.C0[0].cuda(), 2, budget)
-    H.check_assign(Xd, C_prev.cpu().numpy(), lab_s.numpy(), J_s, "fp16", tag="streamed")
+    _check_streamed_against_oracle(km, Xp, Xd, p.C0[0], 3, budget, (lab_s, C_s, J_s), tag="streamed")
+
+
+def _check_streamed_against_oracle(km, Xp, Xd, C0, iters, budget, last, *, sample=None, tag=""):
+    """Teacher-forced parity of the streamed path's own results (its
+    accumulate-mode segment sums and fp64 means): the first iteration from C0,
+    and the last of `iters` from the state the streamed path reached before
+    it.  Labels against the oracle's assignment (every row, or a seeded
+    sample plus the full-row inertia property), centroids against the
+    oracle's update from the streamed labels; empty clusters keep the
+    previous centroid bit for bit."""
+    fmt = H.FMT[Xp.dtype]
+    rng = np.random.default_rng(1)
+    rows = None if sample is None or Xp.shape[0] <= sample else np.sort(
+        rng.choice(Xp.shape[0], size=sample, replace=False))
+
+    def one(C_prev, lab, C_new, J, t):
+        Cp = C_prev.cpu().numpy() if isinstance(C_prev, torch.Tensor) else np.asarray(C_prev)
+        rep = H.check_assign(Xd, Cp, lab.numpy(), J, fmt, rows=rows, tag=f"{tag} it{t}")
+        if rows is not None:
+            H.check_inertia_of_labels(Xd, Cp, lab.numpy(), J, fmt, tag=f"{tag} it{t}")
+        Cn, cnt = oracle.update(Xd, lab.numpy(), Cp.astype(np.float64), Cp.shape[0])
+        rms = float(np.sqrt(np.einsum("ij,ij->i", Xd, Xd).mean()))
+        Cg = C_new.cpu().numpy()
+        err = oracle.centroid_rel_err(Cg, Cn, rms)
+        assert err <= H.TOL_CENTROID, f"{tag} it{t}: streamed centroid rel err {err:.3e}"
+        assert np.array_equal(Cg[cnt == 0], Cp[cnt == 0]), f"{tag} it{t}: an empty cluster moved"
+        H.log(f"{tag} it{t}: streamed update ok (centroid err {err:.2e}, empty clusters {int((cnt == 0).sum())}, "
+              f"near-ties excused {rep['excused']})")
+
+    lab1, C1, J1, _ = km.fit_streamed(Xp, C0.cuda(), 1, budget)
+    one(C0, lab1, C1, J1, 0)
+    if iters > 1:
+        _, C_prev, _, _ = km.fit_streamed(Xp, C0.cuda(), iters - 1, budget)
+        lab, C_last, J = last
+        one(C_prev, lab, C_last, J, iters - 1)
 
 
 @pytest.mark.parametrize("last", [500_000, 2_000_000])
@@ -353,7 +386,8 @@ def test_streamed_last_chunk_across_the_tile_size_change(km, last):
                                   weights=None, workload_code=63, seed=last, k=k)
     X, C0 = X[0], C0[0]
     budget = 2 * chunk * d * 2                      # two slots of `chunk` rows: two chunks
-    lab_s, C_s, J_s, hist_s = km.fit_streamed(X.pin_memory(), C0.cuda(), 2, budget, history=True)
+    Xp = X.pin_memory()
+    lab_s, C_s, J_s, hist_s = km.fit_streamed(Xp, C0.cuda(), 2, budget, history=True)
     lab_i, C_i, J_i, hist_i = km.fit(X.cuda(), C0.cuda(), 2, history=True)
     torch.cuda.synchronize()
     assert abs(hist_s[0] - float(hist_i[0, 0])) <= 1e-9 * hist_s[0]
@@ -364,24 +398,66 @@ def test_streamed_last_chunk_across_the_tile_size_change(km, last):
     assert oracle.centroid_rel_err(C_s.cpu().numpy(), C_i.cpu().numpy(), rms) <= 1e-4
     mism = int((lab_s != lab_i.cpu()).sum())
     assert mism <= 1e-4 * n, mism
+    _check_streamed_against_oracle(km, Xp, Xd, C0, 2, budget, (lab_s, C_s, J_s), tag=f"streamed-last{last}")
+
+
+def _first_and_last(km, p, *, sample, tag):
+    """Full-size parity of a workload at its first and last iteration: the
+    oracle checks iteration 0 from C0 and iteration iters-1 from the state the
+    fit reached after iters-1 iterations (teacher-forced, labels on every row
+    or on `sample` seeded rows per instance, update and inertia on every row);
+    the fit's final labels, centroids and inertia equal those stepwise results
+    bit for bit."""
+    fmt = H.FMT[p.X.dtype]
+    X = p.X.cuda()
+    C0 = p.C0.cuda()
+    Xd = [H.decode(p.X[b], fmt) for b in range(p.B)]
+    rng = np.random.default_rng(17)
+    H.check_step(km, X, Xd, C0, fmt, sample=sample, rng=rng, tag=f"{tag} it0")
+    _, C_prev, _, _ = km.fit(X, C0, p.iters - 1)
+    lab, C_last, J, _, _ = H.check_step(km, X, Xd, C_prev, fmt, sample=sample, rng=rng,
+                                        tag=f"{tag} it{p.iters - 1}")
+    lf, Cf, Jf, _ = km.fit(X, C0, p.iters)
+    torch.cuda.synchronize()
+    assert torch.equal(lf, lab) and torch.equal(Cf, C_last) and torch.equal(Jf, J), f"{tag}: fit differs"
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_c4_full(km):
+    """All 8 iterations of the 64 instances, every row, teacher-forced."""
     p = datagen.make("c4")
-    _stats_ok(H.teacher_forced(km, p.X, p.C0, 2, tag="c4", check_fit=False))
+    _stats_ok(H.teacher_forced(km, p.X, p.C0, p.iters, tag="c4", check_fit=True))
 
 
 @pytest.mark.slow
-def test_c2_full_sampled(km):
-    p = datagen.make("c2")
-    _stats_ok(H.teacher_forced(km, p.X, p.C0, 2, sample=16384, tag="c2", check_fit=False))
+@pytest.mark.timeout(900)
+def test_c2_full_first_and_last(km):
+    """Every row's label at iterations 0 and 19 of 20."""
+    _first_and_last(km, datagen.make("c2"), sample=None, tag="c2")
 
 
 @pytest.mark.slow
-def test_c3_full_sampled(km):
-    p = datagen.make("c3")
-    _stats_ok(H.teacher_forced(km, p.X, p.C0, 1, sample=2048, tag="c3", check_fit=False))
+@pytest.mark.timeout(900)
+def test_c3_full_first_and_last(km):
+    """The headline workload (N = 8,388,608, K = 65,536, bf16; the (3 point
+    blocks, 8 waves) assignment): labels of 2^18 seeded rows at iterations 0
+    and 9 of 10, the update and inertia on every row."""
+    _first_and_last(km, datagen.make("c3"), sample=1 << 18, tag="c3")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_c5_scaled_streamed_against_oracle(km):
+    """The out-of-core workload at N = 2^22 (1 GiB of pinned fp16 rows, K =
+    4,096, device slots of 1/16 of X: 16 chunks): first and last of 3
+    iterations against the oracle, labels on 2^18 seeded rows."""
+    p = datagen.make("c5", n=1 << 22)
+    Xp = p.X[0].pin_memory()
+    budget = Xp.numel() * Xp.element_size() // 8
+    lab, C, J, _ = km.fit_streamed(Xp, p.C0[0].cuda(), p.iters, budget, history=True)
+    _check_streamed_against_oracle(km, Xp, H.decode(p.X[0], "fp16"), p.C0[0], p.iters, budget, (lab, C, J),
+                                   sample=1 << 18, tag="c5s")
 
 
 @pytest.mark.parametrize("case", ["c1", "c4"])
@@ -435,10 +511,8 @@ def test_tune_and_every_config_agree(km, dtype, d, tmp_path):
                                   weights=None, workload_code=58, seed=d, k=211)
     X, C = X[0].cuda(), C0[0].cuda()
     pb, waves, ms = km.tune(X, C)
-    rb = d * X.element_size()
-    compiled = [c for c in [(4, 4), (2, 8), (2, 4), (1, 8), (1, 4)]
-                if c == (1, 4) or (c == (1, 8) and rb <= 512) or (c == (2, 4) and rb <= 512)
-                or (c == (2, 8) and rb <= 256) or (c == (4, 4) and rb <= 256)]
+    compiled = km.assign_configs(X.dtype, d)
+    assert (3, 8) in compiled and len(compiled) == 6   # rows of at most 256 bytes here: every configuration
     assert (pb, waves) in compiled and ms > 0
     dt = {"fp32": 0, "fp16": 1, "bf16": 2}[dtype]
     ref = None
@@ -458,6 +532,150 @@ def test_tune_and_every_config_agree(km, dtype, d, tmp_path):
     # the oracle agrees with the (shared) result
     Xd = H.decode(X.cpu(), dtype)
     H.check_assign(Xd, C.cpu().numpy(), ref[0].numpy(), ref[2], dtype, min_d2=ref[1].numpy(), tag=f"tune-{dtype}-{d}")
+
+
+def _force_config(km, tmp_path, dtype, d, n, batch, k, cfg):
+    dt = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[dtype]
+    f = tmp_path / f"cfg_{dt}_{d}_{n}_{batch}_{k}_{cfg[0]}_{cfg[1]}.txt"
+    f.write_text(f"{dt} {d} {n} {batch} {k} {cfg[0]} {cfg[1]}\n")
+    km.tune_load(str(f))
+
+
+def test_three_block_config_ragged_every_row(km, tmp_path):
+    """The (3 point blocks, 8 waves) assignment that the built-in rule takes
+    for long sweeps (the headline workload), forced on a ragged shape: 200,003
+    points (a partial last job of 768 points), K = 300 (a full and a partial
+    centroid tile), bf16, D = 128.  Every row against the oracle, and bit for
+    bit against the (2, 8) configuration; then a teacher-forced iteration."""
+    n, d, k = 200_003, 128, 300
+    X, C0, _, _ = datagen.mixture(n, d, 150, dtype="bf16", center_dist="normal", center_scale=2.0, sigma=0.5,
+                                  weights=datagen.zipf_weights(150, 1.1), workload_code=66, seed=0, k=k)
+    Xc, C = X.cuda(), C0.cuda()
+    got = {}
+    for cfg in [(3, 8), (2, 8)]:
+        _force_config(km, tmp_path, torch.bfloat16, d, n, 1, k, cfg)
+        lab, md, J = km.assign(Xc, C, want_min_d2=True)
+        torch.cuda.synchronize()
+        got[cfg] = (lab.cpu(), md.cpu(), float(J[0]))
+    assert torch.equal(got[(3, 8)][0], got[(2, 8)][0]) and torch.equal(got[(3, 8)][1], got[(2, 8)][1])
+    assert abs(got[(3, 8)][2] - got[(2, 8)][2]) <= 1e-12 * got[(2, 8)][2]
+    Xd = H.decode(X[0], "bf16")
+    rep = H.check_assign(Xd, C0[0].numpy(), got[(3, 8)][0][0].numpy(), got[(3, 8)][2], "bf16",
+                         min_d2=got[(3, 8)][1][0].numpy(), tag="pb3")
+    H.log(f"pb3 every row: near-ties excused {rep['excused']}")
+    _force_config(km, tmp_path, torch.bfloat16, d, n, 1, k, (3, 8))
+    _stats_ok(H.teacher_forced(km, X, C0, 2, tag="pb3-fit"))
+
+
+def test_zero_rows_exact(km):
+    """Rows x = 0 (every element): the near-tie tolerance 1e-5 ||x||^2 is zero
+    there, so their labels must equal the oracle's exactly; their distance is
+    ||c||^2 of the chosen centroid."""
+    for dtype, d in [("bf16", 128), ("fp16", 64), ("fp32", 32)]:
+        X, C0, _, _ = datagen.mixture(20_000, d, 40, dtype=dtype, center_dist="normal", center_scale=2.0,
+                                      sigma=1.0, weights=None, workload_code=67, seed=d, k=97)
+        X = X.clone()
+        zero = np.arange(0, 20_000, 97)
+        X[0, zero] = 0
+        labels, md, J = km.assign(X.cuda(), C0.cuda(), want_min_d2=True)
+        torch.cuda.synchronize()
+        Xd = H.decode(X[0], dtype)
+        Ch = oracle.round_to_format(C0[0].numpy().astype(np.float64), dtype)
+        lab_o, dmin = oracle.assign(Xd[zero], Ch)
+        assert np.array_equal(labels[0].cpu().numpy()[zero], lab_o), f"{dtype}: a zero row's label differs"
+        assert np.allclose(md[0].cpu().numpy()[zero], dmin, rtol=1e-6, atol=0), f"{dtype}: zero-row distance"
+        _stats_ok(H.teacher_forced(km, X, C0, 2, tag=f"zero-{dtype}"))
+
+
+@pytest.mark.parametrize("k", [256, 257])
+def test_resident_tile_switch(km, k):
+    """K = 256 / 257 at 8 instances of 65,537 points (2,056 jobs of 256
+    points): the built-in rule takes the resident-tile form with all K
+    centroids in one 256-row tile at K = 256, and (2 blocks, 8 waves) with a
+    second, one-row tile at K = 257.  Both against the oracle on every row."""
+    X, C0, _, _ = datagen.mixture(65_537, 128, 64, dtype="fp16", center_dist="normal", center_scale=1.0, sigma=0.3,
+                                  weights=None, workload_code=68, seed=k, k=k, batch=8)
+    _stats_ok(H.teacher_forced(km, X, C0, 2, tag=f"res-K{k}"))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("k", [8191, 8192])
+def test_long_sweep_switch(km, k, tmp_path):
+    """K = 8191 / 8192 at N = 3,145,729 (4,097 jobs of 768 points): the
+    built-in rule takes (3 blocks, 8 waves) from K = 8192 and (2, 8) below.
+    Labels on 2^15 seeded rows against the oracle, the update and inertia on
+    every row, and the picked configuration bit for bit against the other."""
+    n = 3_145_729
+    X, C0, _, _ = datagen.mixture(n, 128, 4096, dtype="bf16", center_dist="normal", center_scale=2.0, sigma=0.5,
+                                  weights=datagen.zipf_weights(4096, 1.1), workload_code=69, seed=k, k=k)
+    Xc, C = X.cuda(), C0.cuda()
+    lab, md, J = km.assign(Xc, C, want_min_d2=True)
+    other = (2, 8) if k == 8192 else (3, 8)
+    _force_config(km, tmp_path, torch.bfloat16, 128, n, 1, k, other)
+    lab2, md2, J2 = km.assign(Xc, C, want_min_d2=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lab, lab2) and torch.equal(md, md2), f"K={k}: configurations disagree"
+    assert abs(float(J[0]) - float(J2[0])) <= 1e-12 * float(J[0])
+    Xd = [H.decode(X[0], "bf16")]
+    H.check_step(km, Xc, Xd, C, "bf16", sample=1 << 15, rng=np.random.default_rng(k), tag=f"sweep-K{k}")
+
+
+def test_k_equals_n_through_fit(km):
+    """K = N distinct bf16 rows of D = 128 with C0 = X, through kmeans_fit:
+    every row is its own cluster, so labels are the identity, the inertia is
+    exactly 0 and every centroid stays its row."""
+    X, _, _, _ = datagen.mixture(1500, 128, 1500, dtype="bf16", center_dist="normal", center_scale=3.0, sigma=1.0,
+                                 weights=None, workload_code=70, seed=0)
+    Xu = torch.unique(X[0].float(), dim=0)
+    Xu = Xu[torch.randperm(Xu.shape[0], generator=torch.Generator().manual_seed(1))]
+    Xb = Xu.to(torch.bfloat16)
+    C0 = Xb.float()
+    labels, C, J, hist = km.fit(Xb.cuda(), C0.cuda(), 3, history=True)
+    torch.cuda.synchronize()
+    assert torch.equal(labels.cpu(), torch.arange(Xb.shape[0], dtype=torch.int32))
+    assert torch.equal(C.cpu(), C0) and float(J[0]) == 0.0 and float(hist.abs().max()) == 0.0
+
+
+def test_fit_replay_follows_a_new_tuning_entry(km, tmp_path, monkeypatch):
+    """A fit captured under one assignment configuration, then a tuning-table
+    entry that selects another for the same shape: the next fit with the same
+    arguments runs the new configuration, equal bit for bit to direct
+    launches of it.  Labels and centroids do not depend on the configuration;
+    the inertia does through its per-workgroup partial sums (128 rows per
+    workgroup against 768) once those fp64 sums are inexact, so the rows here
+    are scaled by powers of two over a range wider than fp64's precision."""
+    n, d, k, iters = 100_003, 32, 200, 3
+    X, C0, _, _ = datagen.mixture(n, d, 50, dtype="fp32", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                  weights=None, workload_code=71, seed=0, k=k)
+    scale = torch.pow(2.0, torch.randint(-30, 31, (n, 1), generator=torch.Generator().manual_seed(5)).float())
+    X = (X[0] * scale)[None].contiguous()
+    C0 = X[:, :k].clone()
+    Xc, C = X[0].cuda(), C0[0].cuda()
+    ws = torch.empty(km.workspace_bytes(n, d, k, 1, torch.float32), dtype=torch.uint8, device="cuda")
+    out = (torch.empty(n, dtype=torch.int32, device="cuda"), torch.empty_like(C),
+           torch.empty(1, dtype=torch.float64, device="cuda"), torch.empty((iters, 1), dtype=torch.float64,
+                                                                          device="cuda"))
+
+    def direct():
+        monkeypatch.setenv("FLASHKM_FIT_GRAPH", "0")
+        r = km.fit(Xc, C, iters, history=True, ws=ws)
+        torch.cuda.synchronize()
+        monkeypatch.delenv("FLASHKM_FIT_GRAPH")
+        return [t.clone() for t in r]
+
+    res = {}
+    for cfg in [(1, 4), (3, 8)]:
+        _force_config(km, tmp_path, torch.float32, d, n, 1, k, cfg)
+        ref = direct()
+        got = km.fit(Xc, C, iters, history=True, ws=ws, out=out)   # same arguments every time
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), f"config {cfg}: the fit differs from direct launches of that configuration"
+        res[cfg] = ref
+    assert torch.equal(res[(1, 4)][0], res[(3, 8)][0]) and torch.equal(res[(1, 4)][1], res[(3, 8)][1])
+    # the two configurations are distinguishable, so a stale replay would have failed above
+    assert not torch.equal(res[(1, 4)][3], res[(3, 8)][3]), "inertia history identical across configurations"
 
 
 def test_resident_tile_batched_agrees(km, tmp_path):
