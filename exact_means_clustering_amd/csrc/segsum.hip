@@ -4,8 +4,8 @@
 // contention on hot clusters).
 //
 // After the argsort, cluster k owns the contiguous sorted positions
-// [off[k], off[k+1]).  The sorted order is cut into fixed chunks of kSegRows
-// positions, one wave each:
+// [off[k], off[k+1]).  The sorted order is cut into fixed chunks of
+// seg_rows(n) positions, one wave each:
 //   level 1  a wave writes the segment offsets off[k] of the segments that
 //            start in its chunk, then sums, per segment piece inside the
 //            chunk, the gathered rows X[perm[j]] in fp32 (4 rows per 64-lane
@@ -75,29 +75,52 @@ __device__ __forceinline__ void finish(const SegOut& o, int64_t k, int lane, con
 // ---------------------------------------------------------------------------
 // level 1: streaming gather + fp32 segmented sums per chunk
 // ---------------------------------------------------------------------------
-// One wave per chunk of kSegRows sorted positions.  The chunk's keys and row
-// ids are staged in LDS; the wave walks the chunk in steps of SL rows (one
-// row per lane slot q, LPR lanes per row) and keeps kRing steps of row loads
-// in flight whatever the segment boundaries.  Each lane slot accumulates its
-// rows of the current segment in fp32; when the (wave-uniform) key changes,
-// the slots are combined in a fixed butterfly and the piece is emitted:
-// finished on the spot if the whole segment lies in the chunk, otherwise
-// stored as the chunk's fragment (slot 0: the chunk's first segment, slot 1:
-// its last).
+// One wave per chunk of U sorted positions.  The wave walks the chunk in
+// steps of SL rows (one row per lane slot q, LPR lanes per row) and keeps
+// kRing steps of row loads in flight whatever the segment boundaries.  Each
+// lane slot accumulates its rows of the current segment in fp32; when the
+// (wave-uniform) key changes, the slots are combined in a fixed butterfly
+// and the piece is emitted: finished on the spot if the whole segment lies
+// in the chunk, otherwise stored as the chunk's fragment (slot 0: the
+// chunk's first segment, slot 1: its last).
 //
-// The staging is transposed, [q][step], so a lane reads the row ids and keys
-// of four consecutive steps of its slot with one 16-byte LDS load.  Entries
-// past the chunk's end (the ring runs kRing steps ahead) hold the key
-// kNoKey and the chunk's last row id: every row load is issued
-// unconditionally (no branch around the loads keeps each ring slot in fixed
-// registers) and a step past the end adds zeros.
+// The chunk's keys and row ids are staged in LDS, wave-private (the kernel
+// has no workgroup barrier), transposed as [q][step] so a lane reads the key
+// and the row id of its slot's step with one LDS load each; a step's are read
+// one step before they are needed.  The staging covers the ring's lookahead
+// past the chunk: entries past the chunk's end hold its last row (every row
+// load is issued unconditionally, which keeps each ring slot in fixed
+// registers); whether a lane's row is real is decided by its position, and a
+// row past the end adds zeros.
+//
+// The memory counter waits: a ring slot's row is consumed before the slot
+// is refilled at the end of its step, so the ring keeps fixed registers
+// across rounds (an old value still live while the slot's next load is in
+// flight makes the register allocator rotate the ring at the loop edge, which
+// needs every load to have landed), and no global store is issued inside the
+// loop over a step's segment boundaries (the compiler would wait for every
+// load in flight before that loop): the loop only waits for the oldest row.
 #ifndef FKM_RING
 constexpr int kRing = 8;   // steps of row loads kept in flight per wave
 #else
 constexpr int kRing = FKM_RING;
 #endif
-constexpr uint32_t kNoKey = 0xFFFFFFFFu;   // no cluster key takes this value
-constexpr int kBuf = 8;                    // finished pieces buffered per wave
+
+// Staging geometry of a level-1 chunk of U rows.
+template <class T, int D, int U>
+struct L1Geo {
+  static constexpr int LPR = D * T::SZ / 16;                   // lanes per row
+  static constexpr int SL = 64 / LPR;                          // rows per step (lane slots)
+  static constexpr int NS = U / SL;                            // steps per chunk
+  // staged steps per slot: the chunk's rounds, the ring's lookahead, and the
+  // one step further that the last step reads ahead
+  static constexpr int NSP = (NS + kRing - 1) / kRing * kRing + kRing + 1;
+  static constexpr int ENT = SL * NSP;                         // staged rows
+  // finished pieces buffered per wave: one step can finish up to SL of them,
+  // and the buffer is drained between steps once it could not take SL more
+  static constexpr int BUF = SL >= 4 ? 2 * SL : 8;
+  static_assert(LPR >= 1 && LPR <= 64 && U % SL == 0, "row and chunk sizes");
+};
 
 // ACC selects accumulate mode (o.S_acc / o.n_acc) at compile time, so the
 // means-mode instance carries no read-modify-write code in its loop.
@@ -106,18 +129,9 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
                                                          const uint2* __restrict__ kv, int64_t n, uint32_t nseg,
                                                          int32_t* __restrict__ off, SegOut o,
                                                          float* __restrict__ frag) {
+  using G = L1Geo<T, D, U>;
   constexpr int VEC = Vec<T>::N;           // elements per 16-byte word
-  constexpr int LPR = D * T::SZ / 16;      // lanes per row
-  constexpr int SL = 64 / LPR;             // rows per step (lane slots)
-  constexpr int NS = U / SL;               // steps per full chunk
-  // Staged steps per slot.  The loop runs whole rounds of kRing steps, and
-  // step i of a round reads the row ids of step i + kRing (four steps per
-  // 16-byte load), so the staging must cover roundup(NS, kRing) + kRing
-  // steps: entries past the chunk hold kNoKey and the chunk's last row.
-  constexpr int NSP = (NS + kRing - 1) / kRing * kRing + kRing;
-  static_assert(LPR >= 1 && LPR <= 64 && U % SL == 0, "row size");
-  static_assert(kRing % 4 == 0 && NS % 4 == 0, "steps are read four at a time");
-  static_assert(NSP % 4 == 0 && NSP >= NS + kRing, "the staging covers every step the ring reads");
+  constexpr int LPR = G::LPR, SL = G::SL, NSP = G::NSP, kBuf = G::BUF;
   __shared__ __align__(16) uint32_t tkey[4][SL][NSP];
   __shared__ __align__(16) uint32_t trow[4][SL][NSP];
   __shared__ __align__(16) float bsum[4][kBuf][D];
@@ -129,32 +143,24 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t c = (int64_t)blockIdx.x * 4 + w;
   const int64_t r0 = c * U;
-  const bool active = r0 < n;
-  const int cnt = active ? (int)(n - r0 < U ? n - r0 : U) : 0;
-  for (int e = lane; e < SL * NSP; e += 64) {
-    const int qq = e / NSP, ii = e - qq * NSP;
-    const int rr = ii * SL + qq;  // row of the chunk
-    uint32_t key = kNoKey, row = 0;
-    if (cnt > 0) {
-      const uint2 v = kv[r0 + (rr < cnt ? rr : cnt - 1)];
-      key = rr < cnt ? v.x : kNoKey;
-      row = v.y;
-    }
-    tkey[w][qq][ii] = key;
-    trow[w][qq][ii] = row;
-  }
-  __syncthreads();
-  if (!active) return;
-  const int q = lane / LPR, g = lane % LPR;
-  auto key_at = [&](int r) -> uint32_t { return tkey[w][r % SL][r / SL]; };  // key of chunk row r
-  const uint32_t kf = __builtin_amdgcn_readfirstlane(key_at(0));
-  const uint32_t kl = __builtin_amdgcn_readfirstlane(key_at(cnt - 1));
-  const int64_t kbefore = r0 > 0 ? (int64_t)kv[r0 - 1].x : -1;  // key of the row before the chunk
-  // does the chunk's first (last) segment continue from the previous (into the next) chunk?
-  const bool cont_left = kbefore == (int64_t)kf;
-  const bool cont_right = r0 + cnt < n && kv[r0 + cnt].x == kl;
-  const int nsteps = (cnt + SL - 1) / SL;
+  if (r0 >= n) return;                     // every access below is wave-private: no barrier to reach
+  const int cnt = (int)(n - r0 < U ? n - r0 : U);
 
+  // Staging: chunk row e (rows at or past cnt read row cnt-1) goes to step
+  // e / SL of slot e % SL; lane l stages rows l + 64 j (coalesced loads).
+  const int64_t kbefore = r0 > 0 ? (int64_t)kv[r0 - 1].x : -1;  // key of the row before the chunk
+  // key of the row after the chunk (the last row's own key if there is none)
+  const uint32_t kafter = kv[r0 + cnt < n ? r0 + cnt : r0 + cnt - 1].x;
+#pragma unroll 4
+  for (int e = lane; e < G::ENT; e += 64) {
+    const uint2 pr = kv[r0 + (e < cnt ? e : cnt - 1)];
+    tkey[w][e % SL][e / SL] = pr.x;
+    trow[w][e % SL][e / SL] = pr.y;
+  }
+  const uint32_t kf = __builtin_amdgcn_readfirstlane(tkey[w][0][0]);
+  // does the chunk's first segment continue from the previous chunk?
+  const bool cont_left = kbefore == (int64_t)kf;
+  const int q = lane / LPR, g = lane % LPR;
   auto load_row = [&](uint32_t row) -> uint4 {
     return load_nt(reinterpret_cast<const uint4*>(X + (int64_t)row * D) + g);
   };
@@ -164,11 +170,12 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
   uint32_t cur = kf;
   int seg_start = 0;
-  // emit the piece of segment k that ends before row `end` of the chunk
   // Finished pieces wait in a wave-private LDS buffer and are written to
-  // global memory after the loop (or when the buffer fills).  Global stores
-  // share the load counter on this architecture, so a store issued inside
-  // the loop would make the following ring waits also wait for its write
+  // global memory between steps when it is nearly full, and after the loop.
+  // Global stores share the load counter on this architecture: a store
+  // issued inside the loop over a step's segment boundaries would make the
+  // compiler wait for every row load in flight before that loop, and any
+  // store makes the following ring waits also wait for its write
   // acknowledgement.  Entry kinds: 0 = a segment finished in this chunk,
   // 1 / 2 = the chunk's fragment slot 0 / 1.
   int nb = 0;  // buffered pieces (wave-uniform)
@@ -212,17 +219,18 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
     }
     nb = 0;
   };
-  // emit the piece of segment k that ends before row `end` of the chunk
-  auto flush = [&](uint32_t k, int end) {
-    float s[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) s[e] = acc[e];
+  // emit the piece of segment k that ends before row `end` of the chunk;
+  // only the chunk's last segment (the final flush) can continue into the
+  // next chunk, and only its first can come from the previous one
+  auto flush = [&](uint32_t k, int end, bool last) {
+    // the slots' sums combine in place: the accumulators restart at zero
+    float* s = acc;
 #pragma unroll
     for (int o2 = LPR; o2 < 64; o2 <<= 1)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) s[e] += __shfl_xor(s[e], o2);
     const bool left = k == kf && cont_left;
-    const bool right = k == kl && cont_right;
+    const bool right = last && r0 + cnt < n && __builtin_amdgcn_readfirstlane(kafter) == k;
     if (q == 0) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) bsum[w][nb][g * VEC + e] = s[e];
@@ -232,30 +240,26 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
       bkind[w][nb] = (left || right) ? (k == kf ? 1 : 2) : 0;
       bcnt[w][nb] = end - seg_start;
     }
-    if (++nb == kBuf) drain();
+    ++nb;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
     seg_start = end;
   };
 
-  const uint4* rows4 = reinterpret_cast<const uint4*>(&trow[w][q][0]);
-  const uint4* keys4 = reinterpret_cast<const uint4*>(&tkey[w][q][0]);
-  auto pick = [](const uint4& v, int i) -> uint32_t { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
+  const uint32_t* keys = &tkey[w][q][0];   // key of step i: keys[i]
+  const uint32_t* rows = &trow[w][q][0];   // row id of step i: rows[i]
   uint4 ring[kRing];
 #pragma unroll
-  for (int u = 0; u < kRing; u += 4) {
-    const uint4 r4 = rows4[u / 4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) ring[u + t] = load_row(pick(r4, t));
-  }
+  for (int u = 0; u < kRing; ++u) ring[u] = load_row(rows[u]);
 
   // Segment offsets (while the first row loads are in flight).  A row whose
-  // key k differs from the previous row's key kp starts segment k:
-  // off[kk] = its position for every kk in (kp, k] (keys no row carries get
-  // the start of the next present key), and the last row of the order also
-  // sets off[kk] = n for kk in (k, nseg].  A lane fills a short range itself;
+  // key k differs from the previous row's key kp starts segment k: off[kk] =
+  // its position for every kk in (kp, k] (keys no row carries get the start
+  // of the next present key), and the last row of the order also sets
+  // off[kk] = n for kk in (k, nseg].  A lane fills a short range itself;
   // ranges of 64 or more keys are filled by the whole wave, one coalesced
   // store per 64 keys.
+  auto key_at = [&](int r) -> uint32_t { return tkey[w][r % SL][r / SL]; };  // key of chunk row r
   for (int e0 = 0; e0 < cnt; e0 += 64) {
     const int e = e0 + lane;
     int64_t a = 0, b = -1, a2 = 0, b2 = -1;
@@ -283,22 +287,21 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
     }
   }
 
-  // Steps are taken kRing at a time; the steps past the chunk's end in the
-  // last round add zeros to the (unchanged) last segment.
+  // Rounds of kRing steps; the steps past the chunk's end in the last round
+  // add zeros to the (unchanged) last segment.
+  const int nsteps = (cnt + SL - 1) / SL;
+  uint32_t mk_next = keys[0], rn_next = rows[kRing];
   for (int i0 = 0; i0 < nsteps; i0 += kRing) {
-    uint4 knext, rnext;
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
-      const int i = i0 + u;
-      if (u % 4 == 0) {
-        knext = keys4[i / 4];                 // keys of steps i .. i+3
-        rnext = rows4[(i + kRing) / 4];       // row ids of steps i+kRing .. i+kRing+3
-      }
-      const uint32_t mk = pick(knext, u % 4);
-      const bool valid = mk != kNoKey;
+      const int i = i0 + u;                   // step
+      const int row0 = i * SL;                // chunk row of the step's slot 0
+      const uint32_t mk = mk_next, rn = rn_next;
+      mk_next = keys[i + 1];
+      rn_next = rows[i + 1 + kRing];
+      const bool valid = row0 + q < cnt;
       uint4 v = ring[u];
-      ring[u] = load_row(pick(rnext, u % 4));
-      const int nv = cnt - i * SL;            // valid rows in this step (uniform)
+      const int nv = cnt - row0;              // valid rows in this step (uniform)
       // key of the step's last valid row (uniform); no valid row: no boundary
       const uint32_t lk = nv > 0 ? __builtin_amdgcn_readlane(mk, ((nv < SL ? nv : SL) - 1) * LPR) : cur;
       if (lk == cur) {
@@ -308,17 +311,19 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
       } else {
         // the step ends `cur` and starts one or more new segments
         for (;;) {
-          Vec<T>::add_if(v, acc, mk == cur);
+          Vec<T>::add_if(v, acc, valid && mk == cur);
           if (cur == lk) break;
           const uint64_t above = __ballot(valid && mk > cur);
           const int fl = __ffsll((unsigned long long)above) - 1;
-          flush(cur, i * SL + fl / LPR);
+          flush(cur, row0 + fl / LPR, false);
           cur = __builtin_amdgcn_readlane(mk, fl);
         }
+        if (nb > kBuf - SL) drain();
       }
+      ring[u] = load_row(rn);
     }
   }
-  flush(cur, cnt);
+  flush(cur, cnt, true);
   drain();
 }
 
