@@ -20,7 +20,8 @@ import os
 import torch
 
 __all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "assign_top2", "assign_soft", "gauss_sum", "seed", "update",
-           "fit", "fit_streamed", "tune", "tune_save", "tune_load", "assign_configs", "DTYPES"]
+           "fit", "fit_streamed", "tune", "tune_save", "tune_load", "assign_configs", "assign_noalloc",
+           "DTYPES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libflashkm.so"
@@ -50,6 +51,8 @@ def _load(path=None):
     lib.kmeans_workspace_bytes.restype = sz
     lib.kmeans_assign.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, P, sz, P]
     lib.kmeans_assign.restype = ctypes.c_int
+    lib.kmeans_assign_noalloc.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, P]
+    lib.kmeans_assign_noalloc.restype = ctypes.c_int
     lib.kmeans_update.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, P, sz, P]
     lib.kmeans_update.restype = ctypes.c_int
     lib.kmeans_fit.argtypes = [P, i32, i64, i32, i32, P, i32, i32, P, P, P, P, P, sz, P]
@@ -186,6 +189,28 @@ def assign(X, C, *, want_min_d2: bool = False, ws=None, stream=None, labels=None
     _check(_lib.kmeans_assign(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(labels), _ptr(md), _ptr(inertia),
                               _ptr(ws), ws_bytes, _stream(stream)))
     return labels, md, inertia
+
+
+@_on_tensor_device
+def assign_noalloc(X, C, *, labels, inertia, min_d2=None, stream=None):
+    """Assignment stage into caller tensors with no workspace and no allocation (the library's static
+    scratch; calls that overlap on one GPU race): labels int32 [.., N], inertia fp64 [B], min_d2 fp32 [.., N]
+    or None.  Returns (labels, min_d2, inertia)."""
+    _need(X, "X")
+    _need(C, "C", torch.float32, like=X)
+    B, N, D = _shape3(X)
+    K = _rows(C, "C", B, D)
+    dt = _dtype(X)
+    _need(labels, "labels", torch.int32, like=X)
+    _count(labels, "labels", B * N)
+    _need(inertia, "inertia", torch.float64, like=X)
+    _count(inertia, "inertia", B)
+    if min_d2 is not None:
+        _need(min_d2, "min_d2", torch.float32, like=X)
+        _count(min_d2, "min_d2", B * N)
+    _check(_lib.kmeans_assign_noalloc(_ptr(X), dt, N, D, B, _ptr(C), K, _ptr(labels), _ptr(min_d2), _ptr(inertia),
+                                      _stream(stream)))
+    return labels, min_d2, inertia
 
 
 @_on_tensor_device

@@ -193,9 +193,70 @@ int fit_graph(const FitArgs& a, Work& w, hipStream_t s) {
   return KM_OK;
 }
 
+// ---- the assignment stage without a caller workspace ------------------------
+// Scratch of kmeans_assign_noalloc: the rounded centroids, their biases and
+// the per-workgroup inertia partials live in this file-scope device array
+// (one copy per GPU, held until the process ends).  Host code never uses
+// the array's name as an address: the per-device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kNoAllocScratch = (size_t)32 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+
+// Regions of the scratch for an assignment of this shape (256-byte aligned).
+struct NoAllocLayout {
+  size_t chat, hb, part, total;
+};
+NoAllocLayout noalloc_layout(int64_t N, int D, int K, int B, int dt) {
+  NoAllocLayout L{};
+  size_t o = 0;
+  L.chat = o;  o = al256(o + (size_t)B * K * D * dtype_size(dt));
+  L.hb = o;    o = al256(o + (size_t)B * kpad(K) * 4);
+  L.part = o;  o = al256(o + (size_t)B * assign_max_wgs(N) * 8);
+  L.total = o;
+  return L;
+}
+
+int scratch_address(void** out) {
+  static std::mutex m;
+  static void* addr[64] = {};
+  int dev = 0;
+  KM_HIP(hipGetDevice(&dev), "device query");
+  if (dev < 0 || dev >= 64) return fail(KM_EINVAL, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(m);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    KM_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch symbol address");
+    if (!p) return fail(KM_EHIP, "scratch symbol address is null");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return KM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int kmeans_assign_noalloc(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B, const float* C, int32_t K,
+                          int32_t* labels, float* min_d2, double* inertia, void* stream) {
+  err_buf()[0] = 0;
+  if (int rc = check_shape(dtype, N, D, K, B)) return rc;
+  if (!X || !C || !labels) return fail(KM_EINVAL, "X, C and labels must be non-null");
+  if (!aligned(X, 16) || !aligned(C, 4) || !aligned(labels, 4) || !aligned(min_d2, 4) || !aligned(inertia, 8))
+    return fail(KM_EINVAL, "misaligned pointer (X needs 16 bytes)");
+  const NoAllocLayout L = noalloc_layout(N, D, K, B, dtype);
+  if (L.total > kNoAllocScratch)
+    return fail(KM_EWORKSPACE, "this shape needs %zu bytes of scratch; the static scratch holds %zu", L.total,
+                kNoAllocScratch);
+  void* base = nullptr;
+  if (int rc = scratch_address(&base)) return rc;
+  char* b = static_cast<char*>(base);
+  Work w{};
+  w.chat = b + L.chat;
+  w.hb = reinterpret_cast<float*>(b + L.hb);
+  w.part = reinterpret_cast<double*>(b + L.part);
+  return run_assign(X, dtype, N, D, B, C, K, labels, min_d2, inertia, nullptr, w, (hipStream_t)stream);
+}
 
 size_t kmeans_workspace_bytes(int64_t N, int32_t D, int32_t K, int32_t B, int32_t dtype) {
   if (check_shape(dtype, N, D, K, B) != KM_OK) return 0;

@@ -89,6 +89,23 @@ KM_API int kmeans_assign(const void* X, int32_t dtype, int64_t N, int32_t D, int
                   int32_t* labels, float* min_d2, double* inertia,
                   void* ws, size_t ws_bytes, void* stream);
 
+/* The assignment stage for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): kmeans_assign with the same arguments and results, minus the
+ * workspace.  Its scratch is a 32 MiB array inside the library, one per
+ * GPU, held from the library's load until the process ends: the rounded
+ * centroids (B*K*D*sizeof(dtype) bytes), their biases (B*ceil(K/256)*1 KiB)
+ * and the per-workgroup inertia partials (B*ceil(N/128)*8 bytes), each
+ * rounded up to 256 bytes.  A shape that needs more is rejected with
+ * KM_EWORKSPACE before anything is enqueued.  Nothing is allocated or freed.
+ * Every call on one GPU uses that GPU's single array: calls that overlap on
+ * one GPU (different streams or threads without ordering) race and give
+ * unspecified results.  Every region a call reads is written earlier in the
+ * same call, so no clearing is needed between calls.  Asynchronous. */
+KM_API int kmeans_assign_noalloc(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t B,
+                                 const float* C, int32_t K,
+                                 int32_t* labels, float* min_d2, double* inertia, void* stream);
+
 /* Centroid update stage (sort-inverse update; paper page abstract, "centroid
  * update stage"; article section "Flash-KMeans が変える点", second point).
  *   counts[b,k] = #{i : labels[b,i] = k}

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {
         "kmeans_workspace_bytes", "kmeans_assign", "kmeans_update", "kmeans_fit", "kmeans_fit_streamed",
         "kmeans_assign_top2", "kmeans_assign_soft", "kmeans_gauss_sum", "kmeans_seed", "kmeans_tune", "kmeans_tune_save",
-        "kmeans_tune_load", "kmeans_assign_configs", "kmeans_last_error"}
+        "kmeans_tune_load", "kmeans_assign_configs", "kmeans_assign_noalloc", "kmeans_last_error"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -54,6 +54,7 @@ def _sig(lib):
     lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
     lib.kmeans_tune_load.argtypes = [ctypes.c_char_p]
     lib.kmeans_assign_configs.argtypes = [i32, i32, P, P, i32, P]
+    lib.kmeans_assign_noalloc.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, P]
     lib.kmeans_last_error.restype = ctypes.c_char_p
     return lib
 
@@ -207,3 +208,19 @@ def test_binding_has_no_cpu_fallback():
     assert km.lib_path() == LIB
     src = open(os.path.join(ROOT, "exact_means_clustering_amd", "__init__.py")).read()
     assert "oracle" not in src and "numpy" not in src
+
+
+def test_assign_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """The allocation-free assignment validates on the host before any GPU
+    call: a shape whose rounded centroids alone exceed the 32 MiB static
+    scratch fails with KM_EWORKSPACE, one that fits passes the size check."""
+    lib = _sig(lib)
+    fake = ctypes.c_void_p(1 << 20)    # never dereferenced: rejected before any launch
+    # K = 65,537 bf16 rows of D = 256: 33.6 MB of rounded centroids > 32 MiB
+    rc = lib.kmeans_assign_noalloc(fake, 2, 70000, 256, 1, fake, 65537, fake, None, None, None)
+    assert rc == 3, rc
+    assert b"32" in lib.kmeans_last_error() or b"scratch" in lib.kmeans_last_error()
+    # invalid shapes and pointers keep their usual codes
+    assert lib.kmeans_assign_noalloc(fake, 2, 10, 128, 1, fake, 20, fake, None, None, None) == 1       # K > N
+    assert lib.kmeans_assign_noalloc(fake, 2, 100, 100, 1, fake, 20, fake, None, None, None) == 2      # bad D
+    assert lib.kmeans_assign_noalloc(None, 2, 100, 128, 1, fake, 20, fake, None, None, None) == 1      # null X
