@@ -21,7 +21,7 @@ import torch
 
 __all__ = ["KMeansError", "lib_path", "workspace_bytes", "assign", "assign_top2", "assign_soft", "gauss_sum", "seed", "update",
            "fit", "fit_streamed", "tune", "tune_save", "tune_load", "assign_configs", "assign_noalloc",
-           "DTYPES"]
+           "stream_timeline", "DTYPES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libflashkm.so"
@@ -72,6 +72,8 @@ def _load(path=None):
     lib.kmeans_tune_save.argtypes = [ctypes.c_char_p]
     lib.kmeans_tune_save.restype = ctypes.c_int
     lib.kmeans_assign_configs.argtypes = [i32, i32, P, P, i32, P]
+    lib.kmeans_stream_timeline.argtypes = [P, i32, P]
+    lib.kmeans_stream_timeline.restype = ctypes.c_int
     lib.kmeans_assign_configs.restype = ctypes.c_int
     lib.kmeans_tune_load.argtypes = [ctypes.c_char_p]
     lib.kmeans_tune_load.restype = ctypes.c_int
@@ -384,6 +386,16 @@ def assign_configs(dtype, D: int) -> list:
     if n.value > 8:
         raise KMeansError(KM_EINVAL, f"{n.value} configurations; the binding reads at most 8")
     return [(pb[i], waves[i]) for i in range(n.value)]
+
+
+def stream_timeline():
+    """Per-chunk timeline of the last fit_streamed on this thread: a list of rows (iteration, chunk, copy-in start,
+    copy-in end, compute start, compute end, labels-out start, labels-out end), times in ms from the fit's start."""
+    n = ctypes.c_int32(0)
+    _check(_lib.kmeans_stream_timeline(None, 0, ctypes.byref(n)))
+    buf = (ctypes.c_double * (8 * max(1, n.value)))()
+    _check(_lib.kmeans_stream_timeline(buf, n.value, ctypes.byref(n)))
+    return [tuple(buf[8 * i + j] for j in range(8)) for i in range(n.value)]
 
 
 def tune_load(path: str):

@@ -14,13 +14,27 @@
 
 #include "flashkm.h"
 
+#include <vector>
+
 using namespace fkm;
 
 namespace {
 
+// Per-chunk timeline of the last streamed fit on this thread: rows of
+// kTimelineCols doubles (iteration, chunk, then the start and end in ms,
+// relative to the fit's first event, of the chunk's host-to-device copy,
+// of its compute and of its labels' device-to-host copy).
+constexpr int kTimelineCols = 8;
+constexpr int64_t kTimelineMaxChunks = 16384;  // longer fits record no timeline
+std::vector<double>& timeline() {
+  static thread_local std::vector<double> t;
+  return t;
+}
+
 struct Res {
   hipStream_t cs = nullptr, xs = nullptr;
   hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
+  std::vector<hipEvent_t> marks;  // timing events of the timeline (origin first, then 6 per chunk)
   void* dev[16] = {};
   int ndev = 0;
   void* alloc(size_t bytes) {
@@ -38,6 +52,7 @@ struct Res {
       if (done[i]) (void)hipEventDestroy(done[i]);
       if (freed[i]) (void)hipEventDestroy(freed[i]);
     }
+    for (hipEvent_t e : marks) (void)hipEventDestroy(e);
     if (cs) (void)hipStreamDestroy(cs);
     if (xs) (void)hipStreamDestroy(xs);
   }
@@ -85,6 +100,7 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
   const int64_t nch = (N + chunk - 1) / chunk;
 
   Res r;
+  timeline().clear();
   KS_HIP(hipStreamSynchronize((hipStream_t)stream), "caller stream sync");
   KS_HIP(hipStreamCreateWithFlags(&r.cs, hipStreamNonBlocking), "stream create");
   KS_HIP(hipStreamCreateWithFlags(&r.xs, hipStreamNonBlocking), "stream create");
@@ -122,6 +138,18 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
   Work& w = wf;  // centroid preparation and partials: same offsets in both layouts
 
   const char* xh = (const char*)X_host;
+  // timeline marks: an origin, then per chunk the copy in, the compute and
+  // the labels' copy out, each bracketed by two timing events on its stream
+  const bool record = (int64_t)iters * nch <= kTimelineMaxChunks;
+  auto mark = [&](hipStream_t st) -> int {
+    if (!record) return KM_OK;
+    hipEvent_t e = nullptr;
+    KS_HIP(hipEventCreate(&e), "event create");
+    r.marks.push_back(e);
+    KS_HIP(hipEventRecord(e, st), "event record");
+    return KM_OK;
+  };
+  if (int rc = mark(r.xs)) return rc;
   // both slots start free
   for (int i = 0; i < 2; ++i) KS_HIP(hipEventRecord(r.freed[i], r.xs), "event record");
 
@@ -136,9 +164,11 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
       const int sl = (int)(c & 1);
       const int64_t rows = (c + 1) * chunk <= N ? chunk : N - c * chunk;
       KS_HIP(hipStreamWaitEvent(r.xs, r.freed[sl], 0), "stream wait");
+      if (int rc = mark(r.xs)) return rc;
       KS_HIP(hipMemcpyAsync(xslot[sl], xh + (size_t)c * chunk * row_bytes, (size_t)rows * row_bytes,
                             hipMemcpyHostToDevice, r.xs),
              "H2D copy");
+      if (int rc = mark(r.xs)) return rc;
       KS_HIP(hipEventRecord(r.copied[sl], r.xs), "event record");
       return KM_OK;
     };
@@ -150,6 +180,7 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
       if (c + 1 < nch)
         if (int rc = h2d(c + 1)) return rc;
       KS_HIP(hipStreamWaitEvent(r.cs, r.copied[sl], 0), "stream wait");
+      if (int rc = mark(r.cs)) return rc;
       const AssignConfig cfg = assign_pick(dtype, D, rows, 1, K);
       KS_HIP(launch_assign(dtype, D, cfg, xslot[sl], wc.chat, wc.hb, rows, K, 1, lslot[sl], nullptr, wc.part, r.cs),
              "assign launch");
@@ -160,10 +191,13 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
       SegOut so{nullptr, nullptr, nullptr, S_acc, n_acc};
       KS_HIP(launch_segment_reduce(dtype, D, xslot[sl], sorted, wc.off, rows, (uint32_t)K, so, wc.seg, r.cs),
              "segment reduce launch");
+      if (int rc = mark(r.cs)) return rc;
       KS_HIP(hipEventRecord(r.done[sl], r.cs), "event record");
       KS_HIP(hipStreamWaitEvent(r.xs, r.done[sl], 0), "stream wait");
+      if (int rc = mark(r.xs)) return rc;
       KS_HIP(hipMemcpyAsync(labels_host + c * chunk, lslot[sl], (size_t)rows * 4, hipMemcpyDeviceToHost, r.xs),
              "labels D2H copy");
+      if (int rc = mark(r.xs)) return rc;
       KS_HIP(hipEventRecord(r.freed[sl], r.xs), "event record");
     }
     KS_HIP(launch_mean_from_sums(S_acc, n_acc, D, K, Cs, C_out, r.cs), "mean launch");
@@ -172,5 +206,50 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
   KS_HIP(hipStreamSynchronize(r.xs), "copy stream sync");
   KS_HIP(hipMemcpy(inertia_host, J_dev + (iters - 1), 8, hipMemcpyDeviceToHost), "inertia copy");
   if (inertia_hist_host) KS_HIP(hipMemcpy(inertia_hist_host, J_dev, (size_t)iters * 8, hipMemcpyDeviceToHost), "inertia copy");
+  if (record) {
+    // marks: origin, then per chunk in issue order: the next chunk's copy in
+    // (issued before this chunk's compute, except chunk 0 of an iteration,
+    // issued first), compute start / end, labels out start / end
+    std::vector<double>& tl = timeline();
+    tl.assign((size_t)iters * nch * kTimelineCols, 0.0);
+    size_t m = 1;
+    auto ms = [&](size_t i, double* out) -> int {
+      float v = 0.f;
+      KS_HIP(hipEventElapsedTime(&v, r.marks[0], r.marks[i]), "event elapsed time");
+      *out = v;
+      return KM_OK;
+    };
+    for (int t = 0; t < iters; ++t) {
+      for (int64_t c = 0; c < nch; ++c) {
+        double* row = &tl[((size_t)t * nch + c) * kTimelineCols];
+        row[0] = t;
+        row[1] = (double)c;
+      }
+      // chunk 0's copy in, then per chunk: [chunk c+1's copy in], compute, labels out
+      if (int rc = ms(m++, &tl[(size_t)t * nch * kTimelineCols + 2])) return rc;
+      if (int rc = ms(m++, &tl[(size_t)t * nch * kTimelineCols + 3])) return rc;
+      for (int64_t c = 0; c < nch; ++c) {
+        double* row = &tl[((size_t)t * nch + c) * kTimelineCols];
+        if (c + 1 < nch) {
+          double* nxt = row + kTimelineCols;
+          if (int rc = ms(m++, &nxt[2])) return rc;
+          if (int rc = ms(m++, &nxt[3])) return rc;
+        }
+        for (int j = 4; j < 8; ++j)
+          if (int rc = ms(m++, &row[j])) return rc;
+      }
+    }
+  }
+  return KM_OK;
+}
+
+extern "C" int kmeans_stream_timeline(double* rows, int32_t cap, int32_t* count) {
+  err_buf()[0] = 0;
+  if (!count || cap < 0 || (cap > 0 && !rows)) return bad(KM_EINVAL, "count must be non-null and rows hold cap rows");
+  const std::vector<double>& tl = timeline();
+  const int64_t n = (int64_t)tl.size() / kTimelineCols;
+  for (int64_t i = 0; i < n && i < cap; ++i)
+    for (int j = 0; j < kTimelineCols; ++j) rows[i * kTimelineCols + j] = tl[(size_t)i * kTimelineCols + j];
+  *count = (int32_t)n;
   return KM_OK;
 }

@@ -161,6 +161,19 @@ KM_API int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N, int
                         int32_t* labels_host, float* C_out, double* inertia_host,
                         double* inertia_hist_host, void* stream);
 
+/* Per-chunk timeline of the last kmeans_fit_streamed call on the calling
+ * thread, to show the copy / compute overlap (article section "Flash-KMeans
+ * が変える点", third point).  One row of 8 doubles per chunk and iteration,
+ * in issue order: iteration, chunk, then the start and end (ms, relative to
+ * the fit's first event, from HIP events recorded on the copy and compute
+ * streams) of the chunk's host-to-device copy, of its compute (assign, sort,
+ * segment sums) and of its labels' device-to-host copy.  The first
+ * min(cap, *count) rows go to `rows` (host, nullable when cap = 0) and
+ * *count receives their number (0 if no streamed fit ran on this thread, or
+ * if it had more than 16,384 chunk iterations, which record no timeline).
+ * Does not touch the GPU. */
+KM_API int kmeans_stream_timeline(double* rows, int32_t cap, int32_t* count);
+
 /* Multi-assignment epilogue (the "Flash-GMM: A Memory-Efficient Kernel for
  * Scalable Soft Clustering" page, abstract: border vectors assigned to more
  * than one cluster).  The assignment kernel with a top-2 running state:

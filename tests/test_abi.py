@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {
         "kmeans_workspace_bytes", "kmeans_assign", "kmeans_update", "kmeans_fit", "kmeans_fit_streamed",
         "kmeans_assign_top2", "kmeans_assign_soft", "kmeans_gauss_sum", "kmeans_seed", "kmeans_tune", "kmeans_tune_save",
-        "kmeans_tune_load", "kmeans_assign_configs", "kmeans_assign_noalloc", "kmeans_last_error"}
+        "kmeans_tune_load", "kmeans_assign_configs", "kmeans_assign_noalloc", "kmeans_stream_timeline",
+        "kmeans_last_error"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -224,3 +225,11 @@ def test_assign_noalloc_rejects_shapes_beyond_its_scratch(lib):
     assert lib.kmeans_assign_noalloc(fake, 2, 10, 128, 1, fake, 20, fake, None, None, None) == 1       # K > N
     assert lib.kmeans_assign_noalloc(fake, 2, 100, 100, 1, fake, 20, fake, None, None, None) == 2      # bad D
     assert lib.kmeans_assign_noalloc(None, 2, 100, 128, 1, fake, 20, fake, None, None, None) == 1      # null X
+
+
+def test_stream_timeline_empty_before_any_streamed_fit(lib):
+    lib.kmeans_stream_timeline.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    n = ctypes.c_int32(-1)
+    assert lib.kmeans_stream_timeline(None, 0, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.kmeans_stream_timeline(None, 4, ctypes.byref(n)) == 1           # cap > 0 without a buffer
+    assert lib.kmeans_stream_timeline(None, 0, None) == 1                      # null count

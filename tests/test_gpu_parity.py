@@ -336,6 +336,16 @@ def test_streamed_matches_in_core(km):
     assert oracle.centroid_rel_err(C_s.cpu().numpy(), C_i.cpu().numpy(), rms) <= 1e-4
     mism = int((lab_s != lab_i.cpu()).sum())
     assert mism <= 1e-4 * X.shape[0], mism
+    # the per-chunk timeline of that 3-iteration fit: 8 chunks per iteration,
+    # each window ordered, a chunk's compute after its copy in, and its
+    # labels out after its compute
+    km.fit_streamed(Xp, p.C0[0].cuda(), 3, budget)
+    tl = km.stream_timeline()
+    assert len(tl) == 3 * 8 and [(int(r[0]), int(r[1])) for r in tl] == [(t, c) for t in range(3) for c in range(8)]
+    eps = 1e-3
+    for r in tl:
+        assert r[2] <= r[3] and r[4] <= r[5] and r[6] <= r[7], r
+        assert r[4] >= r[3] - eps and r[6] >= r[5] - eps, r
     _check_streamed_against_oracle(km, Xp, Xd, p.C0[0], 3, budget, (lab_s, C_s, J_s), tag="streamed")
 
 
