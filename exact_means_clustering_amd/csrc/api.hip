@@ -52,10 +52,7 @@ int run_assign(const void* X, int dt, int64_t N, int D, int B, const float* C, i
   KM_HIP(launch_prep(dt, D, C, w.chat, w.hb, B, K, s), "centroid prep launch");
   const AssignConfig cfg = assign_pick(dt, D, N, B, K);
   KM_HIP(launch_assign(dt, D, cfg, X, w.chat, w.hb, N, K, B, labels, min_d2, w.part, s), "assign launch");
-  if (inertia) {
-    const int64_t nwg = (N + cfg.rows() - 1) / cfg.rows();
-    KM_HIP(launch_inertia_reduce(w.part, (int)nwg, B, inertia, hist, false, s), "inertia launch");
-  }
+  if (inertia) KM_HIP(launch_inertia_reduce(w.part, (int)cfg.parts(N), B, inertia, hist, false, s), "inertia launch");
   return KM_OK;
 }
 
@@ -107,7 +104,7 @@ int enqueue_fit(const FitArgs& a, Work& w, hipStream_t s) {
   const int64_t n = a.N * a.B;
   const uint32_t nseg = (uint32_t)((int64_t)a.B * a.K);
   const AssignConfig cfg = a.cfg;
-  const int64_t nwg = (a.N + cfg.rows() - 1) / cfg.rows();
+  const int64_t nwg = cfg.parts(a.N);
   KM_HIP(launch_prep(a.dt, a.D, a.C0, w.chat, w.hb, a.B, a.K, s), "centroid prep launch");
   for (int t = 0; t < a.iters; ++t) {
     const float* Cs = t == 0 ? a.C0 : a.C_out;
@@ -211,7 +208,7 @@ NoAllocLayout noalloc_layout(int64_t N, int D, int K, int B, int dt) {
   size_t o = 0;
   L.chat = o;  o = al256(o + (size_t)B * K * D * dtype_size(dt));
   L.hb = o;    o = al256(o + (size_t)B * kpad(K) * 4);
-  L.part = o;  o = al256(o + (size_t)B * assign_max_wgs(N) * 8);
+  L.part = o;  o = al256(o + (size_t)B * assign_max_parts(N) * 8);
   L.total = o;
   return L;
 }
@@ -312,8 +309,8 @@ int kmeans_assign_soft(const void* X, int32_t dtype, int64_t N, int32_t D, int32
   KM_HIP(launch_assign_soft(dtype, D, X, w.chat, w.hb, N, K, B, labels, log_density, w.part, sa, s),
          "soft assign launch");
   if (total) {
-    const int64_t nwg = (N + mode_config(dtype, D).rows() - 1) / mode_config(dtype, D).rows();
-    KM_HIP(launch_inertia_reduce(w.part, (int)nwg, B, total, nullptr, false, s), "total launch");
+    KM_HIP(launch_inertia_reduce(w.part, (int)mode_config(dtype, D).parts(N), B, total, nullptr, false, s),
+           "total launch");
   }
   return KM_OK;
 }
@@ -340,8 +337,8 @@ int kmeans_gauss_sum(const void* X, int32_t dtype, int64_t N, int32_t D, int32_t
   const SoftArgs sa{nullptr, 1.4426950408889634f / sigma2, 0.5f / sigma2, wk.wpad};
   KM_HIP(launch_assign_gauss(dtype, D, X, wk.chat, wk.hb, N, K, B, lab, gsum, wk.part, sa, s), "gauss sum launch");
   if (total) {
-    const int64_t nwg = (N + mode_config(dtype, D).rows() - 1) / mode_config(dtype, D).rows();
-    KM_HIP(launch_inertia_reduce(wk.part, (int)nwg, B, total, nullptr, false, s), "total launch");
+    KM_HIP(launch_inertia_reduce(wk.part, (int)mode_config(dtype, D).parts(N), B, total, nullptr, false, s),
+           "total launch");
   }
   return KM_OK;
 }

@@ -160,7 +160,7 @@ __device__ __forceinline__ void improve(const f32x16& acc, float tmax, float& be
 //            sigma2 * log w_k): the best score and index plus the running
 //            sum l = sum_k 2^(t_k - t_best) with t_k = score_k * log2(e) / sigma2;
 //            labels = most responsible component, dist = log density, part =
-//            per-workgroup sums of it;
+//            per-wave sums of it;
 //   kGauss   the same running maximum, and the signed sum
 //            sum_k w_k 2^(t_k - t_best) (weights from the padded array
 //            soft.wpad, staged in LDS with the tile): dist = the Gauss sum
@@ -190,11 +190,6 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
   __shared__ uint4 tile[2][Cfg::TILE_CH];
   __shared__ __align__(16) float tb[2][TK];  // read back as float4
   __shared__ __align__(16) float tw[MODE == kGauss ? 2 : 1][MODE == kGauss ? TK : 4];  // kGauss: weights
-  // per-wave inertia partials, double-buffered by job parity: in the RES form
-  // consecutive jobs need not pass a workgroup barrier between one job's read
-  // of the partials (thread 0) and the next job's writes (every wave); the
-  // barrier of the job in between orders the reuse of a buffer
-  __shared__ double wsum[2][W];
   static_assert(!RES || (MODE == kArgmax && PB == 1 && TK == Cfg::ROWS), "resident tile: one tile, rows = tile rows");
 
   const int tid = threadIdx.x;
@@ -237,8 +232,23 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
   if constexpr (RES) {
     if (jbeg < jend) stage_points(jbeg);
   }
-  int par = 0;  // parity of this workgroup's job count (selects the wsum buffer)
-  for (int64_t job = jbeg; job < jend; job += jstep, par ^= 1) {
+  // RES: a job's results (this lane's label and distance, lane 0's wave
+  // partial) are stored at the next job, after its wait for the staged
+  // points: loads and stores share one counter, so stores issued at the end
+  // of a job would make that wait also wait for their acknowledgement.
+  int64_t pend_o = -1, pend_pi = -1;  // output index of the pending results (-1: none)
+  int pend_l = 0;
+  float pend_d = 0.f;
+  double pend_p = 0.0;
+  auto store_pending = [&]() {
+    if (pend_o >= 0) {
+      labels[pend_o] = pend_l;
+      if (min_d2) min_d2[pend_o] = pend_d;
+    }
+    if (lane == 0 && pend_pi >= 0) part[pend_pi] = pend_p;
+    pend_o = pend_pi = -1;
+  };
+  for (int64_t job = jbeg; job < jend; job += jstep) {
     const int b = (int)(job / nblk);
     const int64_t blk = job - (int64_t)b * nblk;
     const typename T::raw* Xb = X + (int64_t)b * N * D;
@@ -309,6 +319,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
       }
       wait_tile();  // this wave's staged points (and the tile it copied) have landed
       if (fresh) __syncthreads();
+      store_pending();
       const int m = w * 32 + col;
 #pragma unroll
       for (int v = 0; v < HV; ++v) {
@@ -503,11 +514,10 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
     // cancellation): each lane half sums its dims, the halves then add.
     // With a single centroid tile every centroid is still in LDS buffer 0
     // (row k, chunks swizzled as the tile was written), so the row is read
-    // there instead of from global memory.  The workgroup barrier after the
-    // distances (the per-workgroup sum) keeps the next job's tile load from
-    // overwriting the buffer first (RES reloads the tile only for a new
-    // instance, behind a barrier of its own); kTop2 has no such barrier and
-    // reads global memory.
+    // there instead of from global memory.  A workgroup barrier after the
+    // distances keeps the next job's tile load from overwriting the buffer
+    // first (RES reloads the tile only for a new instance, behind a barrier
+    // of its own); kTop2 reads global memory.
     auto direct_d2 = [&](int p, int k) -> float {
       const uint4* cr = reinterpret_cast<const uint4*>(Cb + (int64_t)k * D) + h * HV;
       const bool in_lds = MODE != kTop2 && ntiles == 1;
@@ -573,7 +583,12 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
           bidx[p] = oi;
         }
         const float d2 = direct_d2(p, bidx[p]);
-        if (writer) {
+        if constexpr (RES) {
+          pend_o = writer ? (int64_t)b * N + n : -1;
+          pend_l = bidx[p];
+          pend_d = d2;
+          if (writer) wacc += (double)d2;
+        } else if (writer) {
           labels[(int64_t)b * N + n] = bidx[p];
           if constexpr (MODE == kSoft) {
             // log sum_k w_k exp(-d_k / (2 sigma2)) = a_best + ln(sum_k 2^(t_k - t_best)),
@@ -595,17 +610,20 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
       }
     }
     if constexpr (MODE != kTop2) {
+      // one partial per wave and job, in a fixed place (no atomics, no barrier)
       wacc = wave_sum_f64(wacc);
-      if (lane == 0) wsum[par][w] = wacc;
-      __syncthreads();
-      if (tid == 0) {
-        double tot = 0.0;
-#pragma unroll
-        for (int i = 0; i < W; ++i) tot += wsum[par][i];
-        part[(int64_t)b * nblk + blk] = tot;
+      const int64_t pi = ((int64_t)b * nblk + blk) * W + w;
+      if constexpr (RES) {
+        pend_pi = pi;
+        pend_p = wacc;
+      } else {
+        if (lane == 0) part[pi] = wacc;
+        // the next job reloads tile buffer 0, which direct_d2 read
+        if (ntiles == 1) __syncthreads();
       }
     }
   }
+  if constexpr (RES) store_pending();
 }
 
 // inertia[b] = fixed-order sum of part[b, :], one workgroup per instance

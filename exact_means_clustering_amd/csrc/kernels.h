@@ -20,6 +20,8 @@ struct AssignConfig {
   int pb;
   int waves;
   int rows() const { return waves * 32 * pb; }
+  // inertia partials per instance: one per wave and job of rows() points
+  int64_t parts(int64_t N) const { return (N + rows() - 1) / rows() * waves; }
 };
 // Configuration for a shape (dtype, D, N per instance, B instances, K): the
 // environment variable FLASHKM_ASSIGN_CONFIG="pb,waves" when that pair is
@@ -33,8 +35,9 @@ int assign_configs(int dt, int D, AssignConfig* out, int cap);
 // Tuning table (thread-safe): exact-shape lookup and record.
 bool tune_lookup(int dt, int D, int64_t N, int B, int K, AssignConfig* cfg);
 void tune_record(int dt, int D, int64_t N, int B, int K, AssignConfig cfg);
-// Largest number of assign workgroups per instance over every configuration.
-inline int64_t assign_max_wgs(int64_t N) { return (N + 127) / 128; }
+// Largest number of inertia partials per instance over every configuration
+// (waves * ceil(N / (waves * 32 * pb)) <= ceil(N / 32) + 8).
+inline int64_t assign_max_parts(int64_t N) { return (N + 31) / 32 + 8; }
 
 // Centroid count padded for the bias array: a multiple of every assign tile.
 __host__ __device__ inline int64_t kpad(int K) { return ((int64_t)K + 255) / 256 * 256; }
@@ -44,8 +47,8 @@ __host__ __device__ inline int64_t kpad(int K) { return ((int64_t)K + 255) / 256
 hipError_t launch_prep(int dt, int D, const float* C, void* Chat, float* hb, int64_t B, int K, hipStream_t s,
                        const float* log_w = nullptr, float sigma2 = 0.f);
 
-// Fused distance + running argmin.  part[b * nwg + wg] receives each
-// workgroup's fp64 sum of min_d2 (nwg = ceil(N / rows_per_wg(pb))).
+// Fused distance + running argmin.  part[b * P + j * waves + w] receives wave
+// w's fp64 sum of min_d2 over its points of job j (P = cfg.parts(N)).
 hipError_t launch_assign(int dt, int D, AssignConfig cfg, const void* X, const void* Chat, const float* hb,
                          int64_t N, int K, int B, int32_t* labels, float* min_d2, double* part, hipStream_t s);
 
@@ -86,7 +89,7 @@ hipError_t launch_inertia_reduce(const double* part, int nwg, int B, double* ine
 // The same reduction as extra blocks of another launch (inertia_reduce_block
 // in common.h: one 256-thread workgroup per instance).
 struct InertiaJob {
-  const double* part = nullptr;  // [B, nwg] workgroup partials (null: no job)
+  const double* part = nullptr;  // [B, nwg] per-wave partials (null: no job)
   int nwg = 0;
   int B = 0;
   double* inertia = nullptr;     // [B]

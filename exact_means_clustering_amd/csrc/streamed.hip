@@ -184,8 +184,8 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
       const AssignConfig cfg = assign_pick(dtype, D, rows, 1, K);
       KS_HIP(launch_assign(dtype, D, cfg, xslot[sl], wc.chat, wc.hb, rows, K, 1, lslot[sl], nullptr, wc.part, r.cs),
              "assign launch");
-      const int64_t nwg = (rows + cfg.rows() - 1) / cfg.rows();
-      KS_HIP(launch_inertia_reduce(wc.part, (int)nwg, 1, J_dev + t, nullptr, true, r.cs), "inertia launch");
+      KS_HIP(launch_inertia_reduce(wc.part, (int)cfg.parts(rows), 1, J_dev + t, nullptr, true, r.cs),
+             "inertia launch");
       const uint2* sorted = nullptr;
       KS_HIP(launch_argsort_labels(lslot[sl], rows, 1, K, wc.sort, &sorted, r.cs), "argsort launch");
       SegOut so{nullptr, nullptr, nullptr, S_acc, n_acc};

@@ -37,7 +37,7 @@ inline Layout make_layout(int64_t N, int D, int K, int B, int dt) {
   L.chat = o;  o = al256(o + (size_t)nseg * D * dtype_size(dt));
   L.hb = o;    o = al256(o + (size_t)B * kpad(K) * 4);
   L.wpad = o;  o = al256(o + (size_t)B * kpad(K) * 4);
-  L.part = o;  o = al256(o + (size_t)B * assign_max_wgs(N) * 8);
+  L.part = o;  o = al256(o + (size_t)B * assign_max_parts(N) * 8);
   L.cnt = o;   o = al256(o + (size_t)nseg * 4);
   L.kv0 = o;   o = al256(o + (size_t)n * 8);
   L.kv1 = o;   o = al256(o + (size_t)n * 8);

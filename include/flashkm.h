@@ -95,7 +95,7 @@ KM_API int kmeans_assign(const void* X, int32_t dtype, int64_t N, int32_t D, int
  * workspace.  Its scratch is a 32 MiB array inside the library, one per
  * GPU, held from the library's load until the process ends: the rounded
  * centroids (B*K*D*sizeof(dtype) bytes), their biases (B*ceil(K/256)*1 KiB)
- * and the per-workgroup inertia partials (B*ceil(N/128)*8 bytes), each
+ * and the per-wave inertia partials ((B*ceil(N/32) + 8)*8 bytes), each
  * rounded up to 256 bytes.  A shape that needs more is rejected with
  * KM_EWORKSPACE before anything is enqueued.  Nothing is allocated or freed.
  * Every call on one GPU uses that GPU's single array: calls that overlap on

@@ -650,42 +650,41 @@ def test_k_equals_n_through_fit(km):
 def test_fit_replay_follows_a_new_tuning_entry(km, tmp_path, monkeypatch):
     """A fit captured under one assignment configuration, then a tuning-table
     entry that selects another for the same shape: the next fit with the same
-    arguments runs the new configuration, equal bit for bit to direct
-    launches of it.  Labels and centroids do not depend on the configuration;
-    the inertia does through its per-workgroup partial sums (128 rows per
-    workgroup against 768) once those fp64 sums are inexact, so the rows here
-    are scaled by powers of two over a range wider than fp64's precision."""
-    n, d, k, iters = 100_003, 32, 200, 3
-    X, C0, _, _ = datagen.mixture(n, d, 50, dtype="fp32", center_dist="normal", center_scale=2.0, sigma=1.0,
+    arguments runs the new configuration.  Labels, centroids and inertia do
+    not depend on the configuration, but the caller's workspace shows which
+    one ran (each writes its own number of per-wave inertia partials), so the
+    workspace is filled with a sentinel before every run and must equal, byte
+    for byte, the workspace of direct launches of the configuration in force."""
+    n, d, k, iters = 100_003, 64, 200, 3
+    X, C0, _, _ = datagen.mixture(n, d, 50, dtype="fp16", center_dist="normal", center_scale=2.0, sigma=1.0,
                                   weights=None, workload_code=71, seed=0, k=k)
-    scale = torch.pow(2.0, torch.randint(-30, 31, (n, 1), generator=torch.Generator().manual_seed(5)).float())
-    X = (X[0] * scale)[None].contiguous()
-    C0 = X[:, :k].clone()
     Xc, C = X[0].cuda(), C0[0].cuda()
-    ws = torch.empty(km.workspace_bytes(n, d, k, 1, torch.float32), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(km.workspace_bytes(n, d, k, 1, torch.float16), dtype=torch.uint8, device="cuda")
     out = (torch.empty(n, dtype=torch.int32, device="cuda"), torch.empty_like(C),
            torch.empty(1, dtype=torch.float64, device="cuda"), torch.empty((iters, 1), dtype=torch.float64,
                                                                           device="cuda"))
 
-    def direct():
-        monkeypatch.setenv("FLASHKM_FIT_GRAPH", "0")
-        r = km.fit(Xc, C, iters, history=True, ws=ws)
+    def run(graph):
+        ws.fill_(255)
+        if not graph:
+            monkeypatch.setenv("FLASHKM_FIT_GRAPH", "0")
+        r = km.fit(Xc, C, iters, history=True, ws=ws, out=None if not graph else out)
         torch.cuda.synchronize()
-        monkeypatch.delenv("FLASHKM_FIT_GRAPH")
-        return [t.clone() for t in r]
+        if not graph:
+            monkeypatch.delenv("FLASHKM_FIT_GRAPH")
+        return [t.clone() for t in r], ws.clone()
 
     res = {}
     for cfg in [(1, 4), (3, 8)]:
-        _force_config(km, tmp_path, torch.float32, d, n, 1, k, cfg)
-        ref = direct()
-        got = km.fit(Xc, C, iters, history=True, ws=ws, out=out)   # same arguments every time
-        torch.cuda.synchronize()
+        _force_config(km, tmp_path, torch.float16, d, n, 1, k, cfg)
+        ref, ws_ref = run(graph=False)
+        got, ws_got = run(graph=True)       # same arguments every time
         for a, b in zip(got, ref):
             assert torch.equal(a, b), f"config {cfg}: the fit differs from direct launches of that configuration"
-        res[cfg] = ref
-    assert torch.equal(res[(1, 4)][0], res[(3, 8)][0]) and torch.equal(res[(1, 4)][1], res[(3, 8)][1])
+        assert torch.equal(ws_got, ws_ref), f"config {cfg}: the replayed fit ran another configuration"
+        res[cfg] = ws_ref
     # the two configurations are distinguishable, so a stale replay would have failed above
-    assert not torch.equal(res[(1, 4)][3], res[(3, 8)][3]), "inertia history identical across configurations"
+    assert not torch.equal(res[(1, 4)], res[(3, 8)])
 
 
 def test_resident_tile_batched_agrees(km, tmp_path):
