@@ -182,15 +182,46 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 }
 
 // inertia[b] (+= when accumulating) = fixed-order sum of part[b, 0..nwg) by
-// one 256-thread workgroup: thread t sums part[b, t + 256 i] in order of i,
-// each wave adds its lanes, then thread 0 adds the four wave sums in order.
+// one 256-thread workgroup: thread t sums the pairs part[b, 2 (t + 256 i) + {0, 1}]
+// in order of i into two running sums (one per pair element), adds them, each
+// wave adds its lanes, then thread 0 adds the four wave sums in order.  The
+// pairs are 16-byte loads issued kBatch at a time, so one workgroup reads the
+// ~10^5 partials of a large instance in a few microseconds.
 __device__ __forceinline__ void inertia_reduce_block(const double* __restrict__ part, int nwg, int64_t b,
                                                      double* __restrict__ inertia, double* __restrict__ hist,
                                                      bool accumulate) {
+  constexpr int kBatch = 12;
   __shared__ double ws[4];
-  double v = 0.0;
-#pragma unroll 8
-  for (int i = threadIdx.x; i < nwg; i += 256) v += part[b * nwg + i];
+  const double* p = part + b * nwg;
+  const int n2 = nwg >> 1;
+  double v0 = 0.0, v1 = 0.0;
+  int i = threadIdx.x;
+  if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+    const double2* q = reinterpret_cast<const double2*>(p);
+    for (; i + 256 * (kBatch - 1) < n2; i += 256 * kBatch) {
+      double2 t[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) t[u] = q[i + 256 * u];
+      __builtin_amdgcn_sched_barrier(0);  // every load of the batch issues before the first add
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        v0 += t[u].x;
+        v1 += t[u].y;
+      }
+    }
+    for (; i < n2; i += 256) {
+      const double2 t = q[i];
+      v0 += t.x;
+      v1 += t.y;
+    }
+  } else {
+    for (; i < n2; i += 256) {
+      v0 += p[2 * i];
+      v1 += p[2 * i + 1];
+    }
+  }
+  if ((nwg & 1) && threadIdx.x == 0) v0 += p[nwg - 1];
+  double v = v0 + v1;
   v = wave_sum_f64(v);
   if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
   __syncthreads();

@@ -92,9 +92,17 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
   return m;
 }
 
+// Blocks put in front of the histogram tiles for a side job.
+__host__ __device__ inline int64_t side_blocks(const InertiaJob& side) {
+  return side.part ? ((int64_t)side.B + 7) / 8 * 8 : 0;
+}
+
 // Count d of tile b goes to hist[d * dstride + b * tstride] (digit-major
 // for the scan kernel, tile-major when the scatter sums the counts itself).
-// Blocks past the nblk tiles run the side job (an inertia reduction).
+// The first side.B blocks run the side job (an inertia reduction), so it
+// overlaps the counting instead of trailing it; the tiles start at block
+// side_blocks(side), a multiple of 8, so each tile stays on the XCD it has
+// without a side job.
 // SEG: the n elements are consecutive segments of segN, each cut into ntb
 // tiles of its own (the last one ragged), and the digit is taken from
 // key - segment * kseg, so one pass sorts every segment by its local key.
@@ -105,8 +113,10 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
                                                         Segs seg, InertiaJob side) {
   constexpr uint32_t R = 1u << RB;
   constexpr int DPT = (int)R / kT;  // digits per thread
-  if ((int64_t)blockIdx.x >= nblk) {
-    inertia_reduce_block(side.part, side.nwg, (int64_t)blockIdx.x - nblk, side.inertia, side.hist, false);
+  const int64_t extra = side_blocks(side);
+  if ((int64_t)blockIdx.x < extra) {
+    if ((int64_t)blockIdx.x < side.B)
+      inertia_reduce_block(side.part, side.nwg, (int64_t)blockIdx.x, side.inertia, side.hist, false);
     return;
   }
   __shared__ uint32_t cnt[R];
@@ -114,7 +124,7 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
 #pragma unroll
   for (int j = 0; j < DPT; ++j) cnt[t + kT * j] = 0;
   __syncthreads();
-  const int64_t tile = xcd_tile(blockIdx.x, nblk);
+  const int64_t tile = xcd_tile((int64_t)blockIdx.x - extra, nblk);
   const TilePos p = tile_pos_t<SEG, TILE>(tile, n, seg);
   constexpr int kIPT = TILE / kT;  // keys per thread
   uint32_t d[kIPT];
@@ -318,7 +328,7 @@ template <class Src, int TILE>
 hipError_t one_pass_t(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out, hipStream_t s,
                       const InertiaJob& side) {
   const int64_t nblk = (n + TILE - 1) / TILE;
-  const int64_t extra = side.part ? side.B : 0;
+  const int64_t extra = side_blocks(side);
   const bool scan_free = nblk <= kScanFreeTiles;
   radix_hist_kernel<Src, TILE, false><<<dim3((unsigned)(nblk + extra)), dim3(kT), 0, s>>>(
       src, n, shift, buf.hist, nblk, scan_free ? 1 : nblk, scan_free ? 256 : 1, Segs{}, side);
@@ -345,7 +355,7 @@ hipError_t one_pass(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out,
 template <class Src, int TILE, int RB>
 hipError_t wide_pass_t(Src src, int64_t n, SortBuffers& buf, uint2* out, hipStream_t s, const InertiaJob& side) {
   const int64_t nblk = (n + TILE - 1) / TILE;
-  const int64_t extra = side.part ? side.B : 0;
+  const int64_t extra = side_blocks(side);
   radix_hist_kernel<Src, TILE, false, RB><<<dim3((unsigned)(nblk + extra)), dim3(kT), 0, s>>>(
       src, n, 0, buf.hist, nblk, nblk, 1, Segs{}, side);
   radix_scan_kernel<<<dim3(1u << RB), dim3(kT), 0, s>>>(buf.hist, nblk, buf.dtot);
@@ -369,7 +379,7 @@ hipError_t seg_pass_t(const LabelSrc& src, int64_t N, int B, uint32_t K, SortBuf
   const int64_t n = N * (int64_t)B;
   const Segs sg{N, (N + TILE - 1) / TILE, K};
   const int64_t nblk = sg.ntb * B;
-  const int64_t extra = side.part ? side.B : 0;
+  const int64_t extra = side_blocks(side);
   radix_hist_kernel<LabelSrc, TILE, true><<<dim3((unsigned)(nblk + extra)), dim3(kT), 0, s>>>(
       src, n, 0, buf.hist, nblk, 1, 256, sg, side);
   radix_scatter_kernel<LabelSrc, TILE, false, true><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(
