@@ -100,11 +100,17 @@ __device__ __forceinline__ void finish(const SegOut& o, int64_t k, int lane, con
 // needs every load to have landed), and no global store is issued inside the
 // loop over a step's segment boundaries (the compiler would wait for every
 // load in flight before that loop): the loop only waits for the oldest row.
-#ifndef FKM_RING
-constexpr int kRing = 8;   // steps of row loads kept in flight per wave
+// Steps of row loads kept in flight per wave: 4 for the 512-row chunks of
+// large problems (update of 2^23 bf16 rows of 128 into 65,536 clusters:
+// 0.516 against 0.519-0.520 ms with 8), 8 for the small chunks.
+template <int U>
+constexpr int ring_steps() {
+#ifdef FKM_RING
+  return FKM_RING;
 #else
-constexpr int kRing = FKM_RING;
+  return U >= 512 ? 4 : 8;
 #endif
+}
 
 // Staging geometry of a level-1 chunk of U rows.
 template <class T, int D, int U>
@@ -112,13 +118,16 @@ struct L1Geo {
   static constexpr int LPR = D * T::SZ / 16;                   // lanes per row
   static constexpr int SL = 64 / LPR;                          // rows per step (lane slots)
   static constexpr int NS = U / SL;                            // steps per chunk
+  static constexpr int kRing = ring_steps<U>();
   // staged steps per slot: the chunk's rounds, the ring's lookahead, and the
   // one step further that the last step reads ahead
   static constexpr int NSP = (NS + kRing - 1) / kRing * kRing + kRing + 1;
   static constexpr int ENT = SL * NSP;                         // staged rows
   // finished pieces buffered per wave: one step can finish up to SL of them,
   // and the buffer is drained between steps once it could not take SL more
-  static constexpr int BUF = SL >= 4 ? 2 * SL : 8;
+  // (two more for the 512-row chunks: 0.503 against 0.507 ms for the update
+  // of 2^23 bf16 rows of 128 into 65,536 clusters)
+  static constexpr int BUF = SL >= 4 ? 2 * SL + (U >= 512 ? 2 : 0) : 8;
   static_assert(LPR >= 1 && LPR <= 64 && U % SL == 0, "row and chunk sizes");
 };
 
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
                                                          float* __restrict__ frag) {
   using G = L1Geo<T, D, U>;
   constexpr int VEC = Vec<T>::N;           // elements per 16-byte word
-  constexpr int LPR = G::LPR, SL = G::SL, NSP = G::NSP, kBuf = G::BUF;
+  constexpr int LPR = G::LPR, SL = G::SL, NSP = G::NSP, kBuf = G::BUF, kRing = G::kRing;
   __shared__ __align__(16) uint32_t tkey[4][SL][NSP];
   __shared__ __align__(16) uint32_t trow[4][SL][NSP];
   __shared__ __align__(16) float bsum[4][kBuf][D];
@@ -246,46 +255,52 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
     seg_start = end;
   };
 
+  // Segment offsets.  A row whose key k differs from the previous row's key
+  // kp starts segment k: off[kk] = its position for every kk in (kp, k]
+  // (keys no row carries get the start of the next present key), and the
+  // last row of the order also sets off[kk] = n for kk in (k, nseg].  A lane
+  // fills a short range itself; ranges of 64 or more keys are filled by the
+  // whole wave, one coalesced store per 64 keys.  Large chunks write them
+  // after their rows: a store issued before a ring wait makes that wait also
+  // wait for the store's acknowledgement (0.507 against 0.514 ms for the
+  // same update).  Small chunks write them while their first rows load
+  // (their loop is too short to hide the stores at the end).
+  auto key_at = [&](int r) -> uint32_t { return tkey[w][r % SL][r / SL]; };  // key of chunk row r
+  auto write_offsets = [&]() {
+    for (int e0 = 0; e0 < cnt; e0 += 64) {
+      const int e = e0 + lane;
+      int64_t a = 0, b = -1, a2 = 0, b2 = -1;
+      int32_t val = 0;
+      if (e < cnt) {
+        const int64_t k = key_at(e);
+        const int64_t kp = e > 0 ? (int64_t)key_at(e - 1) : kbefore;
+        val = (int32_t)(r0 + e);
+        if (k != kp) a = kp + 1, b = k;
+        if (r0 + e == n - 1) a2 = k + 1, b2 = nseg;
+      }
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int64_t lo = pass ? a2 : a, hi = pass ? b2 : b;
+        const int32_t v = pass ? (int32_t)n : val;
+        const bool longr = hi - lo >= 64;
+        if (!longr)
+          for (int64_t kk = lo; kk <= hi; ++kk) off[kk] = v;
+        for (uint64_t lm = __ballot(longr); lm; lm &= lm - 1) {
+          const int l = __ffsll((unsigned long long)lm) - 1;
+          const int64_t la = __shfl(lo, l), lb = __shfl(hi, l);
+          const int32_t lv = __shfl(v, l);
+          for (int64_t kk = la + lane; kk <= lb; kk += 64) off[kk] = lv;
+        }
+      }
+    }
+  };
+
   const uint32_t* keys = &tkey[w][q][0];   // key of step i: keys[i]
   const uint32_t* rows = &trow[w][q][0];   // row id of step i: rows[i]
   uint4 ring[kRing];
 #pragma unroll
   for (int u = 0; u < kRing; ++u) ring[u] = load_row(rows[u]);
-
-  // Segment offsets (while the first row loads are in flight).  A row whose
-  // key k differs from the previous row's key kp starts segment k: off[kk] =
-  // its position for every kk in (kp, k] (keys no row carries get the start
-  // of the next present key), and the last row of the order also sets
-  // off[kk] = n for kk in (k, nseg].  A lane fills a short range itself;
-  // ranges of 64 or more keys are filled by the whole wave, one coalesced
-  // store per 64 keys.
-  auto key_at = [&](int r) -> uint32_t { return tkey[w][r % SL][r / SL]; };  // key of chunk row r
-  for (int e0 = 0; e0 < cnt; e0 += 64) {
-    const int e = e0 + lane;
-    int64_t a = 0, b = -1, a2 = 0, b2 = -1;
-    int32_t val = 0;
-    if (e < cnt) {
-      const int64_t k = key_at(e);
-      const int64_t kp = e > 0 ? (int64_t)key_at(e - 1) : kbefore;
-      val = (int32_t)(r0 + e);
-      if (k != kp) a = kp + 1, b = k;
-      if (r0 + e == n - 1) a2 = k + 1, b2 = nseg;
-    }
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int64_t lo = pass ? a2 : a, hi = pass ? b2 : b;
-      const int32_t v = pass ? (int32_t)n : val;
-      const bool longr = hi - lo >= 64;
-      if (!longr)
-        for (int64_t kk = lo; kk <= hi; ++kk) off[kk] = v;
-      for (uint64_t lm = __ballot(longr); lm; lm &= lm - 1) {
-        const int l = __ffsll((unsigned long long)lm) - 1;
-        const int64_t la = __shfl(lo, l), lb = __shfl(hi, l);
-        const int32_t lv = __shfl(v, l);
-        for (int64_t kk = la + lane; kk <= lb; kk += 64) off[kk] = lv;
-      }
-    }
-  }
+  if constexpr (U < 512) write_offsets();
 
   // Rounds of kRing steps; the steps past the chunk's end in the last round
   // add zeros to the (unchanged) last segment.
@@ -325,6 +340,7 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
   }
   flush(cur, cnt, true);
   drain();
+  if constexpr (U >= 512) write_offsets();
 }
 
 // ---------------------------------------------------------------------------
