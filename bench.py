@@ -151,7 +151,8 @@ def assign_traffic(name, B, N, D, K):
 
 def probe(args):
     """Counter-collection target: a plain 1 GiB device copy (calibrates
-    FETCH_SIZE / WRITE_SIZE) followed by one assign and one update."""
+    FETCH_SIZE / WRITE_SIZE) followed by one assign and one update (and, with
+    --zipf-update, one more update with Zipf(1.1) labels)."""
     import torch
 
     import datagen
@@ -169,6 +170,9 @@ def probe(args):
     ws = torch.empty(km.workspace_bytes(p.N, p.D, p.K, p.B, X.dtype), dtype=torch.uint8, device="cuda")
     labels, _, _ = km.assign(X, C, ws=ws)
     km.update(X, labels, C, ws=ws)
+    if args.zipf_update:  # then one update with the Zipf(1.1) labels of --zipf-update
+        zl = torch.from_numpy(datagen.zipf_labels(p.N, p.K, 1.1, seed=3, batch=p.B)).cuda()
+        km.update(X, zl if p.B > 1 else zl[0], C, ws=ws)
     torch.cuda.synchronize()
     print(json.dumps({"probe": args.config, "B": p.B, "N": p.N, "D": p.D, "K": p.K,
                       "assign_source_sha256": assign_source_sha()}), flush=True)
