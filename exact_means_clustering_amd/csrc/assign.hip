@@ -168,13 +168,16 @@ __device__ __forceinline__ void improve(const f32x16& acc, float tmax, float& be
 //            labels = the nearest source.
 enum AssignMode : int { kArgmax = 0, kTop2 = 1, kSoft = 2, kGauss = 3 };
 
-// RES (argmax, one point block, 8 waves, all K centroids in one tile): a
-// workgroup takes a contiguous run of jobs, so consecutive jobs share an
-// instance and its centroid tile stays in LDS; the second tile buffer then
-// stages points instead: each wave copies its next job's 32 rows there
-// (global->LDS, XOR-swizzled like the tile) while it computes the current
-// job, so a job starts from LDS instead of waiting on HBM.  Products, their
-// order and the epilogue are those of the plain (1, 8) configuration.
+// RES (argmax, 8 waves, all K centroids in one tile): a workgroup takes a
+// contiguous run of jobs, so consecutive jobs share an instance and its
+// centroid tile stays in LDS (reloaded, behind a barrier, only where the run
+// enters the next instance), and a job needs no workgroup barrier.  With one
+// point block per wave the second tile buffer stages points instead: each
+// wave copies its next job's 32 rows there (global->LDS, XOR-swizzled like
+// the tile) while it computes the current job, so a job starts from LDS
+// instead of waiting on HBM.  With two blocks (512 points, too many to stage)
+// the points load straight into registers, as in the plain kernel.  Products,
+// their order and the epilogue are those of the plain configuration.
 template <class T, int D, int PB, int W, int MODE, bool RES = false>
 __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* __restrict__ X,
                                                         const typename T::raw* __restrict__ Ch,
@@ -190,7 +193,8 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
   __shared__ uint4 tile[2][Cfg::TILE_CH];
   __shared__ __align__(16) float tb[2][TK];  // read back as float4
   __shared__ __align__(16) float tw[MODE == kGauss ? 2 : 1][MODE == kGauss ? TK : 4];  // kGauss: weights
-  static_assert(!RES || (MODE == kArgmax && PB == 1 && TK == Cfg::ROWS), "resident tile: one tile, rows = tile rows");
+  static_assert(!RES || (MODE == kArgmax && (PB > 1 || TK == Cfg::ROWS)),
+                "resident tile: argmax only; one point block stages a job's rows in a tile buffer");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -228,25 +232,44 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
                                        16, 0, 0);
     }
   };
+  // point fragments straight from global memory: lane half h of the wave's
+  // block p takes dims [h*D/2, (h+1)*D/2) of point p0 + 32 p + col (rows past
+  // N read row N-1; their results are not written)
+  auto load_points = [&](const typename T::raw* Xb, int64_t p0, uint4 (&xf)[PB][HV]) {
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      int64_t n = p0 + p * 32 + col;
+      n = n < N ? n : N - 1;
+      const uint4* src = reinterpret_cast<const uint4*>(Xb + n * D) + h * HV;
+#pragma unroll
+      for (int v = 0; v < HV; ++v) xf[p][v] = src[v];
+    }
+  };
   int cur_b = -1;
-  if constexpr (RES) {
+  if constexpr (RES && PB == 1) {
     if (jbeg < jend) stage_points(jbeg);
   }
   // RES: a job's results (this lane's label and distance, lane 0's wave
   // partial) are stored at the next job, after its wait for the staged
   // points: loads and stores share one counter, so stores issued at the end
   // of a job would make that wait also wait for their acknowledgement.
-  int64_t pend_o = -1, pend_pi = -1;  // output index of the pending results (-1: none)
-  int pend_l = 0;
-  float pend_d = 0.f;
+  int64_t pend_o[PB], pend_pi = -1;  // output index of the pending results (-1: none)
+  int pend_l[PB];
+  float pend_d[PB];
+#pragma unroll
+  for (int p = 0; p < PB; ++p) pend_o[p] = -1, pend_l[p] = 0, pend_d[p] = 0.f;
   double pend_p = 0.0;
   auto store_pending = [&]() {
-    if (pend_o >= 0) {
-      labels[pend_o] = pend_l;
-      if (min_d2) min_d2[pend_o] = pend_d;
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      if (pend_o[p] >= 0) {
+        labels[pend_o[p]] = pend_l[p];
+        if (min_d2) min_d2[pend_o[p]] = pend_d[p];
+      }
+      pend_o[p] = -1;
     }
     if (lane == 0 && pend_pi >= 0) part[pend_pi] = pend_p;
-    pend_o = pend_pi = -1;
+    pend_pi = -1;
   };
   for (int64_t job = jbeg; job < jend; job += jstep) {
     const int b = (int)(job / nblk);
@@ -317,27 +340,23 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
         issue_tile(0, 0);
         cur_b = b;
       }
-      wait_tile();  // this wave's staged points (and the tile it copied) have landed
+      if constexpr (PB > 1) load_points(Xb, p0, xf);
+      wait_tile();  // this wave's points (staged or loaded) and the tile it copied have landed
       if (fresh) __syncthreads();
       store_pending();
-      const int m = w * 32 + col;
+      if constexpr (PB == 1) {
+        const int m = w * 32 + col;
 #pragma unroll
-      for (int v = 0; v < HV; ++v) {
-        const int c = h * HV + v;
-        xf[0][v] = tile[1][m * NCH + (c ^ (m & (NCH - 1)))];
+        for (int v = 0; v < HV; ++v) {
+          const int c = h * HV + v;
+          xf[0][v] = tile[1][m * NCH + (c ^ (m & (NCH - 1)))];
+        }
+        // the reads above complete before the next job's rows overwrite the slice
+        __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */
+        if (job + 1 < jend) stage_points(job + 1);
       }
-      // the reads above complete before the next job's rows overwrite the slice
-      __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */
-      if (job + 1 < jend) stage_points(job + 1);
     } else {
-#pragma unroll
-      for (int p = 0; p < PB; ++p) {
-        int64_t n = p0 + p * 32 + col;
-        n = n < N ? n : N - 1;
-        const uint4* src = reinterpret_cast<const uint4*>(Xb + n * D) + h * HV;
-#pragma unroll
-        for (int v = 0; v < HV; ++v) xf[p][v] = src[v];
-      }
+      load_points(Xb, p0, xf);
       issue_tile(0, 0);
       wait_tile();
       __syncthreads();
@@ -503,7 +522,7 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
           reduce_group(acc, base, wv);
         }
       }
-      if constexpr (!RES) {  // (RES: the single tile stays; the staged rows are waited for at the next job)
+      if constexpr (!RES) {  // (RES: the single tile stays; the next job waits for its own points)
         wait_tile();
         __syncthreads();
       }
@@ -584,9 +603,9 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
         }
         const float d2 = direct_d2(p, bidx[p]);
         if constexpr (RES) {
-          pend_o = writer ? (int64_t)b * N + n : -1;
-          pend_l = bidx[p];
-          pend_d = d2;
+          pend_o[p] = writer ? (int64_t)b * N + n : -1;
+          pend_l[p] = bidx[p];
+          pend_d[p] = d2;
           if (writer) wacc += (double)d2;
         } else if (writer) {
           labels[(int64_t)b * N + n] = bidx[p];
@@ -711,11 +730,15 @@ hipError_t assign_cfg(AssignConfig c, const void* X, const void* Chat, const flo
                       int32_t* labels, float* min_d2, double* part, SoftArgs soft, hipStream_t s) {
   constexpr int rb = D * T::SZ;
   if constexpr (MODE == kArgmax) {
-    // one point block, 8 waves, all centroids in one 256-row tile: the
-    // resident-tile form of that configuration
+    // one or two point blocks, 8 waves, all centroids in one 256-row tile:
+    // the resident-tile form of that configuration
     if constexpr (rb <= 256 && AssignCfg<T, D, 1, 8>::TK == AssignCfg<T, D, 1, 8>::ROWS) {
       if (c.pb == 1 && c.waves == 8 && K <= AssignCfg<T, D, 1, 8>::TK)
         return assign_t<T, D, 1, 8, MODE, true>(X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
+    }
+    if constexpr (cfg_compiled(T::SZ, rb, 2, 8)) {
+      if (c.pb == 2 && c.waves == 8 && K <= AssignCfg<T, D, 2, 8>::TK)
+        return assign_t<T, D, 2, 8, MODE, true>(X, Chat, hb, N, K, B, labels, min_d2, part, soft, s);
     }
 #define FKM_CASE(PB_, W_)                                                                      \
     if constexpr (cfg_compiled(T::SZ, rb, PB_, W_)) {                                          \
@@ -741,10 +764,16 @@ template <class T, int D>
 hipError_t assign_prime_cfg(AssignConfig c) {
   constexpr int rb = D * T::SZ;
   int slots = 0;
-  // (1, 8) may launch its resident-tile form: query that too
+  // (1, 8) and (2, 8) may launch their resident-tile forms: query those too
   if constexpr (rb <= 256 && AssignCfg<T, D, 1, 8>::TK == AssignCfg<T, D, 1, 8>::ROWS) {
     if (c.pb == 1 && c.waves == 8) {
       const hipError_t e = assign_slots<T, D, 1, 8, kArgmax, true>(&slots);
+      if (e != hipSuccess) return e;
+    }
+  }
+  if constexpr (cfg_compiled(T::SZ, rb, 2, 8)) {
+    if (c.pb == 2 && c.waves == 8) {
+      const hipError_t e = assign_slots<T, D, 2, 8, kArgmax, true>(&slots);
       if (e != hipSuccess) return e;
     }
   }
@@ -851,11 +880,17 @@ AssignConfig assign_pick(int dt, int D, int64_t N, int B, int K) {
   const bool long_sweep = K >= 8192 && (N + 767) / 768 * (int64_t)B >= 4096;
   if (long_sweep && cfg_compiled(sz, rb, 3, 8)) return AssignConfig{3, 8};
   // All centroids in one tile (rows of at most 256 bytes, K <= 256) and at
-  // least 2048 jobs of 256 points: the resident-tile form of (1, 8) keeps
-  // each instance's tile in LDS and stages the next job's points while the
-  // current one computes (measured: 5.6% more fit iterations at 64 instances
-  // of 16,384 points, K = 256; no change at 2^16 points, K = 64).
-  if (rb <= 256 && K <= 256 && (N + 255) / 256 * (int64_t)B >= 2048) return AssignConfig{1, 8};
+  // least 2048 jobs: the resident-tile forms keep each instance's tile in LDS
+  // with no per-job barrier.  With 2048 jobs of 512 points, two point blocks
+  // (half the centroid-fragment reads per MFMA) beat one block with staged
+  // points (64 instances of 16,384 points, K = 256: 0.108-0.120 against
+  // 0.114-0.130 ms); with fewer, one block with the next job's points staged
+  // while the current one computes (5.6% more fit iterations than the plain
+  // kernel at that shape; no change at 2^16 points, K = 64).
+  if (rb <= 256 && K <= 256) {
+    if ((N + 511) / 512 * (int64_t)B >= 2048 && cfg_compiled(sz, rb, 2, 8)) return AssignConfig{2, 8};
+    if ((N + 255) / 256 * (int64_t)B >= 2048) return AssignConfig{1, 8};
+  }
   const AssignConfig order[] = {{2, 8}, {1, 8}, {1, 4}};
   for (const AssignConfig& c : order) {
     if (!cfg_compiled(sz, rb, c.pb, c.waves)) continue;

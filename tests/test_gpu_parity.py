@@ -688,11 +688,13 @@ def test_fit_replay_follows_a_new_tuning_entry(km, tmp_path, monkeypatch):
 
 
 def test_resident_tile_batched_agrees(km, tmp_path):
-    """The resident-tile form of (1 block, 8 waves), taken when all K
-    centroids fit one tile: a workgroup's contiguous run of jobs crosses
-    instance boundaries here (3 instances of 100,003 points, about 4.6 jobs
-    per workgroup), so the tile is reloaded inside the run.  Labels and
-    distances equal the other configurations bit for bit, and the oracle."""
+    """The resident-tile forms of (1 block, 8 waves) and (2 blocks, 8 waves),
+    taken when all K centroids fit one tile: a workgroup's contiguous run of
+    jobs crosses instance boundaries here (3 instances of 100,003 points,
+    about 4.6 jobs of 256 or 2.3 of 512 points per workgroup, the last job of
+    each instance partial), so the tile is reloaded inside the run.  Labels
+    and distances equal the plain (1, 4) configuration bit for bit, and the
+    oracle."""
     n, d, k, batch = 100_003, 64, 200, 3
     X, C0, _, _ = datagen.mixture(n, d, 40, dtype="bf16", center_dist="normal", center_scale=2.0, sigma=1.0,
                                   weights=None, workload_code=64, seed=1, k=k, batch=batch)
@@ -715,15 +717,16 @@ def test_resident_tile_batched_agrees(km, tmp_path):
                        min_d2=ref[1][b].numpy(), tag=f"resident b={b}")
 
 
-def test_fit_with_resident_tile_equals_stepwise(km, tmp_path):
-    """A fit whose assignment runs the resident-tile form (forced through the
-    tuning table for this shape): the captured and replayed fit equals the
-    same iterations as stand-alone calls bit for bit."""
+@pytest.mark.parametrize("pb", [1, 2])
+def test_fit_with_resident_tile_equals_stepwise(km, tmp_path, pb):
+    """A fit whose assignment runs a resident-tile form (one or two point
+    blocks, forced through the tuning table for this shape): the captured and
+    replayed fit equals the same iterations as stand-alone calls bit for bit."""
     n, d, k, batch, iters = 20_011, 64, 100, 3, 3
     X, C0, _, _ = datagen.mixture(n, d, 30, dtype="fp16", center_dist="normal", center_scale=2.0, sigma=1.0,
                                   weights=None, workload_code=65, seed=2, k=k, batch=batch)
-    f = tmp_path / "resident.txt"
-    f.write_text(f"1 {d} {n} {batch} {k} 1 8\n")
+    f = tmp_path / f"resident{pb}.txt"
+    f.write_text(f"1 {d} {n} {batch} {k} {pb} 8\n")
     km.tune_load(str(f))
     Xc, C = X.cuda(), C0.cuda()
     Cs = C.clone()
