@@ -68,3 +68,46 @@ def test_noalloc_assign_rejects_oversized_shapes(km):
     with pytest.raises(km.KMeansError) as e:
         km.assign_noalloc(X, C, labels=lab, inertia=J)
     assert e.value.status == 3
+
+
+def test_noalloc_assign_replays_in_a_captured_graph(km):
+    """A caller under graph capture: the allocation-free assignment captured
+    into a torch CUDA graph (after an eager call has set the library up on
+    this device: scratch address, grid query) and replayed three times, the
+    outputs cleared before each replay and other eager work (a workspace
+    assignment of another shape) plus a synchronisation between replays.
+    Every replay equals the eager call bit for bit."""
+    X, C, _, _ = datagen.mixture(20_011, 64, 40, dtype="bf16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                 weights=None, workload_code=74, seed=2, k=300)
+    X, C = X[0].cuda(), C[0].cuda()
+    lab = torch.empty(X.shape[0], dtype=torch.int32, device="cuda")
+    md = torch.empty(X.shape[0], dtype=torch.float32, device="cuda")
+    J = torch.empty(1, dtype=torch.float64, device="cuda")
+    km.assign_noalloc(X, C, labels=lab, inertia=J, min_d2=md)
+    torch.cuda.synchronize()
+    ref = (lab.clone(), md.clone(), J.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream, as torch asks before a capture
+        km.assign_noalloc(X, C, labels=lab, inertia=J, min_d2=md)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        km.assign_noalloc(X, C, labels=lab, inertia=J, min_d2=md)
+    torch.cuda.synchronize()
+    Xo, Co, _, _ = datagen.mixture(9_001, 128, 30, dtype="fp16", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                   weights=None, workload_code=75, seed=3, k=500)
+    Xo, Co = Xo[0].cuda(), Co[0].cuda()
+    for r in range(3):
+        lab.fill_(-1)
+        md.fill_(-1.0)
+        J.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lab, ref[0]), f"replay {r}: labels differ from the eager call"
+        assert torch.equal(md, ref[1]), f"replay {r}: distances differ from the eager call"
+        assert torch.equal(J, ref[2]), f"replay {r}: inertia differs from the eager call"
+        km.assign(Xo, Co)
+        torch.cuda.synchronize()
