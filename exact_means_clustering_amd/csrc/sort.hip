@@ -40,21 +40,26 @@ struct LabelSrc {
   uint32_t K;     // centroids per instance
   int B;          // instances
   double invN;    // 1.0 / N, for the instance index
-  __device__ __forceinline__ uint2 operator()(int64_t i) const {
-    const int32_t l = labels[i];
+  // key of label value l at position i
+  __device__ __forceinline__ uint32_t key(int32_t l, int64_t i) const {
     const uint32_t lab = (uint32_t)l < K ? (uint32_t)l : K - 1;  // out-of-range labels clamp (caller error)
-    if (B == 1) return make_uint2(lab, (uint32_t)i);
+    if (B == 1) return lab;
     // instance index i / N: a floating estimate corrected to the exact floor
     int64_t b = (int64_t)((double)i * invN);
     if ((b + 1) * N <= i) ++b;
     if (b * N > i) --b;
-    return make_uint2((uint32_t)b * K + lab, (uint32_t)i);
+    return (uint32_t)b * K + lab;
   }
+  __device__ __forceinline__ uint2 operator()(int64_t i) const { return make_uint2(key(labels[i], i), (uint32_t)i); }
 };
 struct PairSrc {
   const uint2* kv;
   __device__ __forceinline__ uint2 operator()(int64_t i) const { return kv[i]; }
 };
+template <class Src>
+constexpr bool is_label_src = false;
+template <>
+constexpr bool is_label_src<LabelSrc> = true;
 
 // Segment geometry of a segmented pass (segN elements per segment, ntb
 // tiles each, key offset kseg per segment); unused by a plain pass.
@@ -128,10 +133,32 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
   const TilePos p = tile_pos_t<SEG, TILE>(tile, n, seg);
   constexpr int kIPT = TILE / kT;  // keys per thread
   uint32_t d[kIPT];
+  bool vec = false;
+  if constexpr (is_label_src<Src> && !SEG && kIPT % 4 == 0) {
+    // a whole tile of 16-byte aligned labels: four labels per load (4-byte
+    // loads move half the bytes per instruction); which thread counts which
+    // key does not matter
+    const int32_t* lp = src.labels + p.row0 + p.first;
+    vec = p.first + TILE <= p.lim && (reinterpret_cast<uintptr_t>(lp) & 15) == 0;
+    if (vec) {
 #pragma unroll
-  for (int r = 0; r < kIPT; ++r) {
-    const int64_t li = p.first + r * kT + t;
-    d[r] = li < p.lim ? ((src(p.row0 + li).x - p.koff) >> shift) & (R - 1) : R;
+      for (int r4 = 0; r4 < kIPT / 4; ++r4) {
+        const int li = (r4 * kT + t) * 4;
+        const int4 l4 = *reinterpret_cast<const int4*>(lp + li);
+        const int64_t i = p.row0 + p.first + li;
+        d[4 * r4 + 0] = ((src.key(l4.x, i) - p.koff) >> shift) & (R - 1);
+        d[4 * r4 + 1] = ((src.key(l4.y, i + 1) - p.koff) >> shift) & (R - 1);
+        d[4 * r4 + 2] = ((src.key(l4.z, i + 2) - p.koff) >> shift) & (R - 1);
+        d[4 * r4 + 3] = ((src.key(l4.w, i + 3) - p.koff) >> shift) & (R - 1);
+      }
+    }
+  }
+  if (!vec) {
+#pragma unroll
+    for (int r = 0; r < kIPT; ++r) {
+      const int64_t li = p.first + r * kT + t;
+      d[r] = li < p.lim ? ((src(p.row0 + li).x - p.koff) >> shift) & (R - 1) : R;
+    }
   }
   // LDS atomics: the counts are exact integers, so their order is irrelevant.
   // When all 64 keys of a wave's round share one digit (a skewed label
@@ -228,10 +255,34 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
   const int64_t first = p.first + (int64_t)w * KW;
   uint2 e[RW];
   uint32_t rr[RW];
+  // First pass: lane l takes the labels of rows 4 (64 r4 + l) + {0..3} of
+  // the wave's quarter, four per 16-byte load where the tile is whole and
+  // aligned (4-byte loads move half the bytes per instruction); they go back
+  // to row order through this wave's quarter of lkv after the histogram
+  // loads are issued.
+  constexpr bool kLab = is_label_src<Src> && !SEG && RW % 4 == 0;
+  int4 l4[kLab ? RW / 4 : 1];
+  if constexpr (kLab) {
+    const int32_t* lp = src.labels + p.row0 + first;
+    const bool vec = p.first + TILE <= p.lim && (reinterpret_cast<uintptr_t>(lp) & 15) == 0;
 #pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int64_t li = first + r * 64 + lane;
-    e[r] = li < p.lim ? src(p.row0 + li) : make_uint2(0u, 0u);
+    for (int r4 = 0; r4 < RW / 4; ++r4) {
+      const int li = (r4 * 64 + lane) * 4;
+      if (vec) {
+        l4[r4] = *reinterpret_cast<const int4*>(lp + li);
+      } else {
+        int v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = first + li + j < p.lim ? lp[li + j] : 0;
+        l4[r4] = make_int4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int64_t li = first + r * 64 + lane;
+      e[r] = li < p.lim ? src(p.row0 + li) : make_uint2(0u, 0u);
+    }
   }
 
   // this tile's first position among, and count of, each digit it owns
@@ -263,6 +314,18 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
     h0[0] = before;
     cn[0] = own;
     dt[0] = all;
+  }
+  if constexpr (kLab) {
+    uint32_t* tw = reinterpret_cast<uint32_t*>(lkv) + w * KW;
+#pragma unroll
+    for (int r4 = 0; r4 < RW / 4; ++r4) *reinterpret_cast<int4*>(tw + (r4 * 64 + lane) * 4) = l4[r4];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int64_t li = first + r * 64 + lane;
+      e[r] = li < p.lim ? make_uint2(src.key((int32_t)tw[r * 64 + lane], p.row0 + li), (uint32_t)(p.row0 + li))
+                        : make_uint2(0u, 0u);
+    }
   }
   uint32_t sdt = 0, scn = 0;
 #pragma unroll
