@@ -60,6 +60,10 @@ template <class Src>
 constexpr bool is_label_src = false;
 template <>
 constexpr bool is_label_src<LabelSrc> = true;
+template <class Src>
+constexpr bool is_pair_src = false;
+template <>
+constexpr bool is_pair_src<PairSrc> = true;
 
 // Segment geometry of a segmented pass (segN elements per segment, ntb
 // tiles each, key offset kseg per segment); unused by a plain pass.
@@ -150,6 +154,20 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
         d[4 * r4 + 1] = ((src.key(l4.y, i + 1) - p.koff) >> shift) & (R - 1);
         d[4 * r4 + 2] = ((src.key(l4.z, i + 2) - p.koff) >> shift) & (R - 1);
         d[4 * r4 + 3] = ((src.key(l4.w, i + 3) - p.koff) >> shift) & (R - 1);
+      }
+    }
+  }
+  if constexpr (is_pair_src<Src> && !SEG && kIPT % 2 == 0) {
+    // a whole tile: two pairs per 16-byte load (the pair buffers are
+    // 256-byte aligned and tiles start at multiples of TILE)
+    vec = p.first + TILE <= p.lim;
+    if (vec) {
+      const uint4* kp = reinterpret_cast<const uint4*>(src.kv + p.row0 + p.first);
+#pragma unroll
+      for (int r2 = 0; r2 < kIPT / 2; ++r2) {
+        const uint4 q = kp[r2 * kT + t];
+        d[2 * r2 + 0] = ((q.x - p.koff) >> shift) & (R - 1);
+        d[2 * r2 + 1] = ((q.z - p.koff) >> shift) & (R - 1);
       }
     }
   }
@@ -255,14 +273,31 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
   const int64_t first = p.first + (int64_t)w * KW;
   uint2 e[RW];
   uint32_t rr[RW];
-  // First pass: lane l takes the labels of rows 4 (64 r4 + l) + {0..3} of
-  // the wave's quarter, four per 16-byte load where the tile is whole and
-  // aligned (4-byte loads move half the bytes per instruction); they go back
-  // to row order through this wave's quarter of lkv after the histogram
-  // loads are issued.
+  // 16-byte loads (narrower loads move fewer bytes per instruction): in the
+  // first pass lane l takes the labels of rows 4 (64 r4 + l) + {0..3} of the
+  // wave's quarter, four per load where the tile is whole and aligned; in
+  // later passes the pairs of rows 2 (64 r2 + l) + {0, 1}, two per load.
+  // They go back to row order through this wave's quarter of lkv after the
+  // histogram loads are issued.
   constexpr bool kLab = is_label_src<Src> && !SEG && RW % 4 == 0;
+  constexpr bool kPair = is_pair_src<Src> && !SEG && RW % 2 == 0;
   int4 l4[kLab ? RW / 4 : 1];
-  if constexpr (kLab) {
+  uint4 q2[kPair ? RW / 2 : 1];
+  if constexpr (kPair) {
+    const uint2* kp = src.kv + p.row0 + first;
+    const bool vec = p.first + TILE <= p.lim;
+#pragma unroll
+    for (int r2 = 0; r2 < RW / 2; ++r2) {
+      const int li = (r2 * 64 + lane) * 2;
+      if (vec) {
+        q2[r2] = *reinterpret_cast<const uint4*>(kp + li);
+      } else {
+        const uint2 a = first + li < p.lim ? kp[li] : make_uint2(0u, 0u);
+        const uint2 b = first + li + 1 < p.lim ? kp[li + 1] : make_uint2(0u, 0u);
+        q2[r2] = make_uint4(a.x, a.y, b.x, b.y);
+      }
+    }
+  } else if constexpr (kLab) {
     const int32_t* lp = src.labels + p.row0 + first;
     const bool vec = p.first + TILE <= p.lim && (reinterpret_cast<uintptr_t>(lp) & 15) == 0;
 #pragma unroll
@@ -314,6 +349,17 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
     h0[0] = before;
     cn[0] = own;
     dt[0] = all;
+  }
+  if constexpr (kPair) {
+    uint2* tw = lkv + w * KW;
+#pragma unroll
+    for (int r2 = 0; r2 < RW / 2; ++r2) *reinterpret_cast<uint4*>(tw + (r2 * 64 + lane) * 2) = q2[r2];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int64_t li = first + r * 64 + lane;
+      e[r] = li < p.lim ? tw[r * 64 + lane] : make_uint2(0u, 0u);
+    }
   }
   if constexpr (kLab) {
     uint32_t* tw = reinterpret_cast<uint32_t*>(lkv) + w * KW;
