@@ -234,6 +234,27 @@ def test_batched_update_skewed_labels(km, n, k, batch):
     H.log(f"batched update n={n} k={k} B={batch}: worst centroid err {worst:.2e}")
 
 
+@pytest.mark.parametrize("n,k", [(20_011, 300), (2_200_011, 5_000)])
+def test_update_misaligned_labels_equal_aligned(km, n, k):
+    """The sort reads labels four per 16-byte load where a tile is whole and
+    aligned, one at a time otherwise: labels at an address 4 bytes past a
+    16-byte boundary (every tile on the second path) give the same centroids
+    and counts bit for bit as the same labels aligned.  Shapes: one
+    wide-digit pass over 1,024-key tiles (K = 300) and two 8-bit passes over
+    4,096-key tiles (K = 5,000), both with a ragged last tile."""
+    X, C0, _, _ = _mixture(n, 64, k, "bf16", seed=31)
+    Xc, C = X[0].cuda(), C0[0].cuda()
+    lab, _, _ = km.assign(Xc, C)
+    buf = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+    lab_m = buf[1:]
+    lab_m.copy_(lab)
+    assert lab_m.data_ptr() % 16 == 4
+    C_a, n_a = km.update(Xc, lab, C)
+    C_m, n_m = km.update(Xc, lab_m, C)
+    torch.cuda.synchronize()
+    assert torch.equal(n_a, n_m) and torch.equal(C_a, C_m)
+
+
 @pytest.mark.parametrize("n,k,batch", [(20_011, 257, 1), (50_000, 2048, 1), (30_001, 300, 2), (9_001, 290, 7)])
 def test_wide_digit_update(km, n, k, batch):
     """Keys of 9 to 11 bits (B*K from 257 to 2048) sort in one pass with a
