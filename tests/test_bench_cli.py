@@ -27,3 +27,23 @@ def test_help_lists_the_measurement_options():
     assert r.returncode == 0
     for opt in ("--steps", "--warmup", "--config", "--epilogue", "--seeding", "--zipf-update", "--tune", "--probe"):
         assert opt in r.stdout, opt
+
+
+def test_stream_overlap_from_a_hand_made_timeline():
+    """The chunked-stream overlap figures from a timeline whose unions and
+    intersections are worked out by hand: copy-in windows [0,2) [1,3) [5,6)
+    (union 4 ms), compute windows [2,4) [2.5,3.5) [6,7) (union 3 ms), labels out [4,4.5) twice and
+    [7,8); copy and compute overlap on [2,3) only (1 ms)."""
+    import bench
+    tl = [[0, 0, 0.0, 2.0, 2.0, 4.0, 4.0, 4.5],
+          [0, 1, 1.0, 3.0, 2.5, 3.5, 4.0, 4.5],
+          [0, 2, 5.0, 6.0, 6.0, 7.0, 7.0, 8.0]]
+    o = bench.stream_overlap(tl, 3, h2d_bytes=4e9)
+    assert o["chunks_recorded"] == 3 and o["chunks_issued"] == 3
+    assert o["wall_ms"] == 8.0
+    assert o["h2d_busy_ms"] == 4.0 and o["compute_busy_ms"] == 3.0 and o["d2h_busy_ms"] == 1.5
+    assert o["both_busy_ms"] == 1.0
+    assert o["h2d_busy_frac"] == 0.5
+    assert abs(o["hidden_frac_of_shorter"] - 1.0 / 3.0) < 1e-12
+    assert abs(o["h2d_gbs_while_copying"] - 1000.0) < 1e-9      # 4 GB in 4 ms
+    assert bench.stream_overlap([], 5, 4e9) == {"chunks_recorded": 0, "chunks_issued": 5}
