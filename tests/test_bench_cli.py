@@ -47,3 +47,23 @@ def test_stream_overlap_from_a_hand_made_timeline():
     assert abs(o["hidden_frac_of_shorter"] - 1.0 / 3.0) < 1e-12
     assert abs(o["h2d_gbs_while_copying"] - 1000.0) < 1e-9      # 4 GB in 4 ms
     assert bench.stream_overlap([], 5, 4e9) == {"chunks_recorded": 0, "chunks_issued": 5}
+
+
+def test_assign_traffic_calibration_and_staleness(tmp_path, monkeypatch):
+    """HBM bytes per assign launch from a counter summary: each counter is
+    scaled by what it read for a plain copy of known size (here FETCH_SIZE
+    read the 1 GiB copy as 512 MiB, so fetches count twice), and the figure is
+    withdrawn (None) for another shape or another assign source."""
+    import bench
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "traffic_cx.txt").write_text(
+        "# header\nB=1\nN=1000\nD=128\nK=64\nassign_source_sha256=abc\ncopy_bytes=1073741824\n"
+        "copy_fetch_kib=524288\ncopy_write_kib=1048576\nassign_fetch_kib=1000\nassign_write_kib=10\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "assign_source_sha", lambda: "abc")
+    assert bench.assign_traffic("cx", 1, 1000, 128, 64) == 1000 * 1024 * 2.0 + 10 * 1024 * 1.0
+    assert bench.assign_traffic("cx", 1, 1001, 128, 64) is None      # another shape
+    assert bench.assign_traffic("cy", 1, 1000, 128, 64) is None      # no summary
+    monkeypatch.setattr(bench, "assign_source_sha", lambda: "def")
+    assert bench.assign_traffic("cx", 1, 1000, 128, 64) is None      # counters taken on another source
