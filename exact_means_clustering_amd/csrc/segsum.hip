@@ -46,9 +46,9 @@ __device__ __forceinline__ void fused_prep(const SegOut& o, int64_t k, int lane,
   }
 }
 
-// Finish a segment: means mode writes C_new / counts (and the fused
-// preparation), accumulate mode adds into S_acc / n_acc.  `v` holds the
-// segment sum for dims lane + 64*j.
+// Finish a segment: means mode writes C_new (and the fused preparation; the
+// counts come from the offsets, in the fill blocks), accumulate mode adds
+// into S_acc / n_acc.  `v` holds the segment sum for dims lane + 64*j.
 template <class T, int D>
 __device__ __forceinline__ void finish(const SegOut& o, int64_t k, int lane, const double* v, int64_t cnt) {
   constexpr int PER = (D + 63) / 64;
@@ -67,7 +67,6 @@ __device__ __forceinline__ void finish(const SegOut& o, int64_t k, int lane, con
       c[j] = d < D ? (float)(v[j] / (double)cnt) : 0.f;
       if (d < D) o.C_new[k * D + d] = c[j];
     }
-    if (lane == 0) o.counts[k] = (int32_t)cnt;
     if (o.chat) fused_prep<T, D>(o, k, lane, c);
   }
 }
@@ -208,9 +207,8 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
           *reinterpret_cast<float4*>(frag + (c * 2 + (kind - 1)) * D + d) = v;
         }
       }
-      if (lane == 0 && kind == 0) {
-        if constexpr (ACC) o.n_acc[k] += nk;
-        else o.counts[k] = nk;
+      if constexpr (ACC) {
+        if (lane == 0 && kind == 0) o.n_acc[k] += nk;
       }
       if constexpr (!ACC) {
         if (kind == 0 && o.chat) {
@@ -346,15 +344,19 @@ __global__ __launch_bounds__(256) void seg_level1_kernel(const typename T::raw* 
 // ---------------------------------------------------------------------------
 // level 2: per group of chunks, combine chunk fragments (fp64)
 // ---------------------------------------------------------------------------
-// Means mode: a cluster no row carries (off[k] == off[k+1]) gets count 0 and
-// keeps its previous centroid (its fused preparation, made from the previous
-// centroid, stays as it is).  One thread per cluster, 256 per block.
+// Means mode: every cluster's count is off[k+1] - off[k], written here for
+// all clusters at once (coalesced, after the gather, so no count store
+// competes with it); a cluster no row carries (count 0) keeps its previous
+// centroid (its fused preparation, made from the previous centroid, stays as
+// it is).  One thread per cluster, 256 per block.
 __device__ __forceinline__ void empty_fill_block(int64_t blk, const int32_t* __restrict__ off, int64_t nseg, int D,
                                                  const float* __restrict__ C_prev, float* __restrict__ C_new,
                                                  int32_t* __restrict__ counts) {
   const int64_t k = blk * 256 + threadIdx.x;
-  if (k >= nseg || off[k] != off[k + 1]) return;
-  counts[k] = 0;
+  if (k >= nseg) return;
+  const int32_t cnt = off[k + 1] - off[k];
+  counts[k] = cnt;
+  if (cnt != 0) return;
   if (C_new != C_prev) {  // D is a multiple of 4: copy the row as float4
     const float4* src = reinterpret_cast<const float4*>(C_prev + k * D);
     float4* dst = reinterpret_cast<float4*>(C_new + k * D);
