@@ -12,9 +12,10 @@
 //            load for D*SZ = 256 B).  A segment that lies inside the chunk is
 //            finished on the spot; the chunk's first / last piece of a
 //            segment that crosses the chunk edge goes to fragment slot 0 / 1.
-//            (Means mode: clusters no row carries are then filled from
-//            C_prev by a separate parallel pass.)
-//   level 2  one wave per group of kSegGroup chunks adds (fp64) the chunk
+//            (Means mode: every cluster's count, off[k+1] - off[k], is then
+//            written, and clusters no row carries are filled from C_prev, by
+//            extra blocks of the level-2 launch, or by a separate pass.)
+//   level 2  one workgroup per group of kSegGroup chunks adds (fp64) the chunk
 //            fragments of every segment that crosses a chunk edge; segments
 //            inside the group are finished, the others leave group fragments.
 //   level 3  the segment (if any) that crosses into a group from the left
