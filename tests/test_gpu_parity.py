@@ -463,9 +463,11 @@ def test_c4_full(km):
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
-def test_c2_full_first_and_last(km):
-    """Every row's label at iterations 0 and 19 of 20."""
-    _first_and_last(km, datagen.make("c2"), sample=None, tag="c2")
+def test_c2_full(km):
+    """All 20 iterations of N = 1,048,576, K = 1,024, fp16, every row,
+    teacher-forced, and the fit equal to the stepwise calls."""
+    p = datagen.make("c2")
+    _stats_ok(H.teacher_forced(km, p.X, p.C0, p.iters, tag="c2", check_fit=True))
 
 
 @pytest.mark.slow
