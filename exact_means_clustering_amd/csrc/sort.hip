@@ -56,6 +56,20 @@ struct PairSrc {
   const uint2* kv;
   __device__ __forceinline__ uint2 operator()(int64_t i) const { return kv[i]; }
 };
+// The high pass of a two-pass sort of keys below 2^16 over fewer than 2^24
+// rows reads 4-byte elements (high key byte << 24 | row) that the low pass
+// wrote in low-byte order: the low byte of the element at position i is the
+// low-digit bucket holding i, found from the low pass's digit totals.  As a
+// plain source it yields the key with its low byte zero, which is all the
+// histogram of the high digit needs.
+struct PackedSrc {
+  const uint32_t* kv;
+  const uint32_t* lo_tot;  // the low pass's 256 digit totals
+  __device__ __forceinline__ uint2 operator()(int64_t i) const {
+    const uint32_t v = kv[i];
+    return make_uint2((v >> 24) << 8, v & 0xFFFFFFu);
+  }
+};
 template <class Src>
 constexpr bool is_label_src = false;
 template <>
@@ -64,6 +78,10 @@ template <class Src>
 constexpr bool is_pair_src = false;
 template <>
 constexpr bool is_pair_src<PairSrc> = true;
+template <class Src>
+constexpr bool is_packed_src = false;
+template <>
+constexpr bool is_packed_src<PackedSrc> = true;
 
 // Segment geometry of a segmented pass (segN elements per segment, ntb
 // tiles each, key offset kseg per segment); unused by a plain pass.
@@ -171,6 +189,23 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
       }
     }
   }
+  if constexpr (is_packed_src<Src> && !SEG && kIPT % 4 == 0) {
+    // a whole tile: four packed elements per 16-byte load, the digit is the
+    // top byte
+    static_assert(RB == 8, "packed elements carry an 8-bit digit");
+    vec = p.first + TILE <= p.lim;
+    if (vec) {
+      const uint4* kp = reinterpret_cast<const uint4*>(src.kv + p.first);
+#pragma unroll
+      for (int r4 = 0; r4 < kIPT / 4; ++r4) {
+        const uint4 q = kp[r4 * kT + t];
+        d[4 * r4 + 0] = q.x >> 24;
+        d[4 * r4 + 1] = q.y >> 24;
+        d[4 * r4 + 2] = q.z >> 24;
+        d[4 * r4 + 3] = q.w >> 24;
+      }
+    }
+  }
   if (!vec) {
 #pragma unroll
     for (int r = 0; r < kIPT; ++r) {
@@ -245,13 +280,17 @@ __global__ __launch_bounds__(kT) void radix_scan_kernel(uint32_t* __restrict__ h
 // RB > 8 (scanned only): a wide digit of up to 11 bits, so a key of that
 // many bits is sorted in one pass; thread t then owns the DPT consecutive
 // digits t*DPT .. t*DPT + DPT - 1 (with 8 bits, digit t).
-template <class Src, int TILE, bool SCANNED, bool SEG, int RB = 8>
+// PACK: the low pass of a two-pass sort of keys below 2^16 over fewer than
+// 2^24 rows writes each element in 4 bytes, (key >> 8) << 24 | row, to out
+// read as 32-bit words (a PackedSrc for the high pass).
+template <class Src, int TILE, bool SCANNED, bool SEG, int RB = 8, bool PACK = false>
 __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, int shift,
                                                            const uint32_t* __restrict__ hist,
                                                            const uint32_t* __restrict__ dtot, int64_t nblk,
                                                            Segs seg, uint2* __restrict__ out) {
   static_assert(!(SCANNED && SEG), "a segmented pass sums its own counts");
   static_assert(RB == 8 || (SCANNED && !SEG), "wide digits use the scanned histogram");
+  static_assert(!is_packed_src<Src> || (SCANNED && !SEG && RB == 8 && !PACK), "packed input: scanned high pass");
   constexpr uint32_t R = 1u << RB;
   constexpr int DPT = (int)R / kT;    // digits per thread
   constexpr int KW = TILE / 4;        // keys per wave
@@ -261,6 +300,7 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
   __shared__ uint32_t lstart[R];      // first LDS slot of digit d
   __shared__ uint32_t wcnt[4][R];     // per-wave digit counts, then per-wave offsets
   __shared__ uint32_t tmp[4];
+  __shared__ uint32_t lo_start[is_packed_src<Src> ? 256 : 1];  // packed input: first position of each low digit
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int64_t g = xcd_tile(blockIdx.x, nblk);  // the tile this workgroup sorts
@@ -281,9 +321,29 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
   // histogram loads are issued.
   constexpr bool kLab = is_label_src<Src> && !SEG && RW % 4 == 0;
   constexpr bool kPair = is_pair_src<Src> && !SEG && RW % 2 == 0;
+  constexpr bool kPk = is_packed_src<Src>;
+  static_assert(!kPk || RW % 4 == 0, "packed input: whole 16-byte loads per lane");
   int4 l4[kLab ? RW / 4 : 1];
   uint4 q2[kPair ? RW / 2 : 1];
-  if constexpr (kPair) {
+  uint4 k4[kPk ? RW / 4 : 1];
+  if constexpr (kPk) {
+    // packed input: lane l takes the elements of rows 4 (64 r4 + l) + {0..3}
+    // of the wave's quarter, like the labels of the first pass
+    const uint32_t* kp = src.kv + first;
+    const bool vec = p.first + TILE <= p.lim;
+#pragma unroll
+    for (int r4 = 0; r4 < RW / 4; ++r4) {
+      const int li = (r4 * 64 + lane) * 4;
+      if (vec) {
+        k4[r4] = *reinterpret_cast<const uint4*>(kp + li);
+      } else {
+        uint32_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = first + li + j < p.lim ? kp[li + j] : 0u;
+        k4[r4] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  } else if constexpr (kPair) {
     const uint2* kp = src.kv + p.row0 + first;
     const bool vec = p.first + TILE <= p.lim;
 #pragma unroll
@@ -350,6 +410,18 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
     cn[0] = own;
     dt[0] = all;
   }
+  // packed input: the low digits' first positions (an exclusive scan of the
+  // low pass's totals), and the low digits of this tile's first and last
+  // positions, which bound every element's low digit
+  uint32_t lo_a = 0, lo_b = 0;
+  if constexpr (kPk) {
+    uint32_t tot;
+    lo_start[t] = block_exclusive_scan_256(src.lo_tot[t], tmp, &tot);
+    __syncthreads();
+    const int64_t last = (p.first + TILE < p.lim ? p.first + TILE : p.lim) - 1;
+    lo_a = (uint32_t)__syncthreads_count(t >= 1 && lo_start[t] <= (uint32_t)p.first);
+    lo_b = (uint32_t)__syncthreads_count(t >= 1 && lo_start[t] <= (uint32_t)last);
+  }
   if constexpr (kPair) {
     uint2* tw = lkv + w * KW;
 #pragma unroll
@@ -371,6 +443,27 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
       const int64_t li = first + r * 64 + lane;
       e[r] = li < p.lim ? make_uint2(src.key((int32_t)tw[r * 64 + lane], p.row0 + li), (uint32_t)(p.row0 + li))
                         : make_uint2(0u, 0u);
+    }
+  }
+  if constexpr (kPk) {
+    uint32_t* tw = reinterpret_cast<uint32_t*>(lkv) + w * KW;
+#pragma unroll
+    for (int r4 = 0; r4 < RW / 4; ++r4) *reinterpret_cast<uint4*>(tw + (r4 * 64 + lane) * 4) = k4[r4];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int64_t li = first + r * 64 + lane;
+      const uint32_t v = tw[r * 64 + lane];
+      // the low digit holding position li: the last digit whose first
+      // position is at most li (an empty digit's first position equals the
+      // next one's, so it is never the last)
+      uint32_t a = lo_a, b = lo_b;
+      while (a < b) {
+        const uint32_t m = (a + b + 1) >> 1;
+        if (lo_start[m] <= (uint32_t)li) a = m;
+        else b = m - 1;
+      }
+      e[r] = li < p.lim ? make_uint2(((v >> 24) << 8) | a, v & 0xFFFFFFu) : make_uint2(0u, 0u);
     }
   }
   uint32_t sdt = 0, scn = 0;
@@ -429,7 +522,9 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
   const int cnt = rem < TILE ? (int)rem : TILE;
   for (int i = t; i < cnt; i += kT) {
     const uint2 v = lkv[i];
-    out[gbase[((v.x - p.koff) >> shift) & (R - 1)] + (uint32_t)i] = v;
+    const uint32_t pos = gbase[((v.x - p.koff) >> shift) & (R - 1)] + (uint32_t)i;
+    if constexpr (PACK) reinterpret_cast<uint32_t*>(out)[pos] = ((v.x >> 8) << 24) | v.y;
+    else out[pos] = v;
   }
 }
 
@@ -457,6 +552,33 @@ hipError_t one_pass(Src src, int64_t n, int shift, SortBuffers& buf, uint2* out,
                     const InertiaJob& side = InertiaJob{}) {
   return sort_tile(n) == kSortTileSmall ? one_pass_t<Src, kSortTileSmall>(src, n, shift, buf, out, s, side)
                                         : one_pass_t<Src, kSortTile>(src, n, shift, buf, out, s, side);
+}
+
+// Two 8-bit passes over n < 2^24 keys below 2^16 (scanned: more than
+// kScanFreeTiles tiles).  The low pass writes each element in 4 bytes (high
+// key byte and row) into kv[0], read as 32-bit words; the high pass reads
+// them, restores the low byte from the element's position, and writes the
+// sorted (key, row) pairs to out.  Half the bytes of the 8-byte intermediate
+// are written, counted and read back.  The low pass's totals stay in
+// dtot[256..511].
+template <int TILE>
+hipError_t packed_two_pass_t(const LabelSrc& ls, int64_t n, SortBuffers& buf, uint2* out, hipStream_t s,
+                             const InertiaJob& side) {
+  const int64_t nblk = (n + TILE - 1) / TILE;
+  const int64_t extra = side_blocks(side);
+  uint32_t* dlo = buf.dtot + 256;
+  radix_hist_kernel<LabelSrc, TILE, false><<<dim3((unsigned)(nblk + extra)), dim3(kT), 0, s>>>(
+      ls, n, 0, buf.hist, nblk, nblk, 1, Segs{}, side);
+  radix_scan_kernel<<<dim3(256), dim3(kT), 0, s>>>(buf.hist, nblk, dlo);
+  radix_scatter_kernel<LabelSrc, TILE, true, false, 8, true><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(
+      ls, n, 0, buf.hist, dlo, nblk, Segs{}, buf.kv[0]);
+  const PackedSrc ps{reinterpret_cast<const uint32_t*>(buf.kv[0]), dlo};
+  radix_hist_kernel<PackedSrc, TILE, false><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(
+      ps, n, 8, buf.hist, nblk, nblk, 1, Segs{}, InertiaJob{});
+  radix_scan_kernel<<<dim3(256), dim3(kT), 0, s>>>(buf.hist, nblk, buf.dtot);
+  radix_scatter_kernel<PackedSrc, TILE, true, false><<<dim3((unsigned)nblk), dim3(kT), 0, s>>>(
+      ps, n, 8, buf.hist, buf.dtot, nblk, Segs{}, out);
+  return hipGetLastError();
 }
 
 // One pass over keys of RB (9 to 11) bits with RB-bit digits: histogram,
@@ -527,6 +649,12 @@ hipError_t launch_argsort_labels(const int32_t* labels, int64_t N, int B, int K,
                       : wide_pass<11>(ls, n, buf, buf.kv[0], s, sj);
   }
   if (256 * sort_blocks(n) > buf.hist_words) return hipErrorInvalidValue;  // workspace laid out for fewer rows
+  if (passes == 2 && n < ((int64_t)1 << 24) && sort_blocks(n) > kScanFreeTiles) {
+    *sorted = buf.kv[1];
+    const InertiaJob sj = side ? *side : InertiaJob{};
+    return sort_tile(n) == kSortTileSmall ? packed_two_pass_t<kSortTileSmall>(ls, n, buf, buf.kv[1], s, sj)
+                                          : packed_two_pass_t<kSortTile>(ls, n, buf, buf.kv[1], s, sj);
+  }
   hipError_t e = one_pass(ls, n, 0, buf, buf.kv[0], s, side ? *side : InertiaJob{});
   if (e != hipSuccess) return e;
   int cur = 0;
