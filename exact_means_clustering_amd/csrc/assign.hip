@@ -536,23 +536,21 @@ __global__ __launch_bounds__(W * 64) void assign_kernel(const typename T::raw* _
     // there instead of from global memory.  A workgroup barrier after the
     // distances keeps the next job's tile load from overwriting the buffer
     // first (RES reloads the tile only for a new instance, behind a barrier
-    // of its own); kTop2 reads global memory.
+    // of its own); kTop2 reads global memory.  The chunks are all loaded
+    // before the first is used, and each half adds its squared differences
+    // with fused multiply-adds in dimension order.
     auto direct_d2 = [&](int p, int k) -> float {
       const uint4* cr = reinterpret_cast<const uint4*>(Cb + (int64_t)k * D) + h * HV;
       const bool in_lds = MODE != kTop2 && ntiles == 1;
-      float part_d = 0.f;
+      uint4 cw[HV];
 #pragma unroll
       for (int v = 0; v < HV; ++v) {
-        float xv[Vec<T>::N], cv[Vec<T>::N];
-        Vec<T>::unpack(xf[p][v], xv);
         const int c = h * HV + v;
-        Vec<T>::unpack(in_lds ? tile[0][k * NCH + (c ^ (k & (NCH - 1)))] : cr[v], cv);
-#pragma unroll
-        for (int e = 0; e < Vec<T>::N; ++e) {
-          const float df = xv[e] - cv[e];
-          part_d += df * df;
-        }
+        cw[v] = in_lds ? tile[0][k * NCH + (c ^ (k & (NCH - 1)))] : cr[v];
       }
+      float part_d = 0.f;
+#pragma unroll
+      for (int v = 0; v < HV; ++v) part_d = Vec<T>::sq_add(xf[p][v], cw[v], part_d);
       const float other = __shfl_xor(part_d, 32);
       return h == 0 ? part_d + other : other + part_d;
     };

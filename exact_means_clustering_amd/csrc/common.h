@@ -85,10 +85,28 @@ struct F32 {
 // exact.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// sq_add(x, c, acc): acc plus the squared differences of the elements of
+// x and c, added with fused multiply-adds in element order (for the 16-bit
+// types each difference is the exact difference rounded once to fp32).
 template <class T> struct Vec;
+template <class T>
+__device__ __forceinline__ float sq_add_unpacked(const uint4& x, const uint4& c, float acc) {
+  float xv[T::N], cv[T::N];
+  T::unpack(x, xv);
+  T::unpack(c, cv);
+#pragma unroll
+  for (int e = 0; e < T::N; ++e) {
+    const float df = xv[e] - cv[e];
+    acc = fmaf(df, df, acc);
+  }
+  return acc;
+}
 template <> struct Vec<BF16> {
   static constexpr int N = 8;
   __device__ static void unpack(const uint4& v, float* o) { BF16::unpack8(v, o); }
+  __device__ __forceinline__ static float sq_add(const uint4& x, const uint4& c, float acc) {
+    return sq_add_unpacked<Vec<BF16>>(x, c, acc);
+  }
   __device__ __forceinline__ static void add_with(const uint4& v, float* acc, uint32_t lo, uint32_t hi) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     const bf16x2 blo = __builtin_bit_cast(bf16x2, lo), bhi = __builtin_bit_cast(bf16x2, hi);
@@ -107,6 +125,30 @@ template <> struct Vec<BF16> {
 template <> struct Vec<F16> {
   static constexpr int N = 8;
   __device__ static void unpack(const uint4& v, float* o) { F16::unpack8(v, o); }
+  // x - c of the low / high halves of two words: a mixed-precision fma
+  // x * 1 + (-c) on the f16 halves, one instruction for the two conversions
+  // and the subtraction, with the same single rounding
+  __device__ __forceinline__ static float diff_lo(uint32_t x, uint32_t c) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,1]" : "=v"(d) : "v"(x), "v"(c));
+    return d;
+  }
+  __device__ __forceinline__ static float diff_hi(uint32_t x, uint32_t c) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(x), "v"(c));
+    return d;
+  }
+  __device__ __forceinline__ static float sq_add(const uint4& x, const uint4& c, float acc) {
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float d0 = diff_lo(xw[i], cw[i]);
+      acc = fmaf(d0, d0, acc);
+      const float d1 = diff_hi(xw[i], cw[i]);
+      acc = fmaf(d1, d1, acc);
+    }
+    return acc;
+  }
   __device__ __forceinline__ static void add_with(const uint4& v, float* acc, uint32_t lo, uint32_t hi) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     const f16x2 blo = __builtin_bit_cast(f16x2, lo), bhi = __builtin_bit_cast(f16x2, hi);
@@ -125,6 +167,9 @@ template <> struct Vec<F16> {
 template <> struct Vec<F32> {
   static constexpr int N = 4;
   __device__ static void unpack(const uint4& v, float* o) { F32::unpack4(v, o); }
+  __device__ __forceinline__ static float sq_add(const uint4& x, const uint4& c, float acc) {
+    return sq_add_unpacked<Vec<F32>>(x, c, acc);
+  }
   __device__ __forceinline__ static void add(const uint4& v, float* acc) {
     acc[0] += __uint_as_float(v.x);
     acc[1] += __uint_as_float(v.y);

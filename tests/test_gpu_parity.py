@@ -935,3 +935,28 @@ def test_update_large_problem_path(km, case):
     err = H.check_update(H.decode(X[0], "fp32"), lab[0], C_prev[0].numpy(), C_new.cpu()[0].numpy(),
                          counts.cpu()[0].numpy(), k, tag=f"large-{case}")
     H.log(f"update large path {case}: centroid err {err:.2e}")
+
+
+@pytest.mark.parametrize("case", ["packed_largest", "pairs_smallest", "two_low_digits"])
+def test_update_two_pass_intermediate(km, case):
+    """Two-pass sorts (keys of 12 to 16 bits) over fewer than 2^24 rows pass
+    4-byte elements (high key byte and row) between the passes and restore
+    the low byte from the position; from 2^24 rows the 8-byte pairs are kept.
+    Against the oracle: the largest row count of the packed form and the
+    smallest of the pair form (Zipf labels over K = 65,536), and labels whose
+    low byte is only 0 or 255, so 254 of the 256 low digits are empty."""
+    k, d = 65_536, 16
+    n = {"packed_largest": (1 << 24) - 1, "pairs_smallest": 1 << 24, "two_low_digits": 300_007}[case]
+    X, _, _, _ = datagen.mixture(n, d, 16, dtype="fp32", center_dist="normal", center_scale=2.0, sigma=1.0,
+                                 weights=None, workload_code=61, seed=1)
+    if case == "two_low_digits":
+        i = np.arange(n)
+        lab = ((i * 7919 % 256) * 256 + np.where(i % 3 == 0, 255, 0)).astype(np.int32)[None]
+    else:
+        lab = datagen.zipf_labels(n, k, 1.1, seed=4)
+    C_prev = torch.randn(1, k, d, generator=torch.Generator().manual_seed(3))
+    C_new, counts = km.update(X.cuda(), torch.from_numpy(lab).cuda(), C_prev.cuda())
+    torch.cuda.synchronize()
+    err = H.check_update(H.decode(X[0], "fp32"), lab[0], C_prev[0].numpy(), C_new.cpu()[0].numpy(),
+                         counts.cpu()[0].numpy(), k, tag=f"two-pass-{case}")
+    H.log(f"update two-pass {case} n={n}: centroid err {err:.2e}")
