@@ -150,7 +150,8 @@ inline int64_t sort_hist_words(int64_t N, int B, int K) {
 }
 
 // Sort elements are (key, row) pairs packed in one 8-byte word, so a pass
-// reads and writes each element with a single access.
+// reads and writes each element with a single access (a two-pass sort below
+// 2^24 rows keeps its intermediate as 4-byte words in the first half of kv[0]).
 struct SortBuffers {
   uint2* kv[2];     // [n] each: ping-pong pair buffers
   uint32_t* hist;   // [hist_words], at least sort_hist_words(N, B, K) for the shape it was laid out for

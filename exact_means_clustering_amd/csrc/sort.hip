@@ -10,7 +10,8 @@
 //           digit base + workgroup offset + rank.
 // Elements travel as (key, row) pairs packed in 8 bytes, so every pass reads
 // and writes each element with one access and a digit run of a tile is one
-// contiguous piece of the output.
+// contiguous piece of the output; between the two passes of keys below 2^16
+// over fewer than 2^24 rows they travel in 4 bytes (high key byte and row).
 // Ranks come from wave-level digit matching (eight ballots give each lane the
 // mask of lanes holding the same digit) and per-wave counters, so the output
 // order is fully determined: equal keys keep their row order.  Histogram
