@@ -481,6 +481,16 @@ def test_c3_full_first_and_last(km):
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
+def test_c3_every_iteration(km):
+    """The headline workload at each of its 10 iterations, teacher-forced:
+    labels of 2^14 seeded rows per iteration, the update and the inertia of
+    the GPU's labels on every row, and the fit equal to the stepwise calls."""
+    p = datagen.make("c3")
+    _stats_ok(H.teacher_forced(km, p.X, p.C0, p.iters, sample=1 << 14, tag="c3", check_fit=True))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_c5_scaled_streamed_against_oracle(km):
     """The out-of-core workload at N = 2^22 (1 GiB of pinned fp16 rows, K =
     4,096, device slots of 1/16 of X: 16 chunks): first and last of 3
