@@ -236,8 +236,7 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
 // One workgroup per digit: exclusive scan of hist[d][0..nblk) in place,
 // dtot[d] = row total.  Each thread takes kScanPer consecutive counts per
 // round (16-byte loads and stores where the row allows), so the 2048 tiles of
-// 2^23 keys are one round (update of 2^23 keys into 65,536 clusters 2-3 us
-// faster than with 4 counts per thread).
+// 2^23 keys are one round.
 constexpr int kScanPer = 8;
 __global__ __launch_bounds__(kT) void radix_scan_kernel(uint32_t* __restrict__ hist, int64_t nblk,
                                                         uint32_t* __restrict__ dtot) {
