@@ -108,16 +108,34 @@ __device__ __forceinline__ TilePos tile_pos_t(int64_t g, int64_t n, const Segs& 
 }
 
 // Mask of the active lanes of this wave whose RB-bit digit equals mine.
+// Per bit, t is all ones where this lane's bit is set, and the lanes whose
+// bit agrees are ~(ballot ^ t), applied to the two 32-bit halves of the mask
+// with one three-input bit operation each (truth table 0x90: src0 & ~(src1 ^
+// src2)): four vector instructions per bit, with every bit's extract and
+// ballot issued ahead of the mask updates.  The empty asm statement keeps
+// the compiler from re-deriving each ballot's condition with a shift.  (A
+// per-lane select between the ballot and its complement cost the compiler
+// nine instructions per bit; the scatter spends most of its issue cycles on
+// the vector ALU.)
 template <int RB>
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
-  uint64_t m = __ballot(valid);
+  const uint64_t v = __ballot(valid);
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  uint32_t t[RB];
+  uint64_t bb[RB];
 #pragma unroll
   for (int bit = 0; bit < RB; ++bit) {
-    const bool on = (d >> bit) & 1u;
-    const uint64_t bb = __ballot(on);
-    m &= on ? bb : ~bb;
+    t[bit] = (uint32_t)__builtin_amdgcn_sbfe((int)d, bit, 1);
+    asm volatile("" : "+v"(t[bit]));
   }
-  return m;
+#pragma unroll
+  for (int bit = 0; bit < RB; ++bit) bb[bit] = __ballot(t[bit] != 0u);
+#pragma unroll
+  for (int bit = 0; bit < RB; ++bit) {
+    lo = __builtin_amdgcn_bitop3_b32(lo, (uint32_t)bb[bit], t[bit], 0x90);
+    hi = __builtin_amdgcn_bitop3_b32(hi, (uint32_t)(bb[bit] >> 32), t[bit], 0x90);
+  }
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Blocks put in front of the histogram tiles for a side job.
