@@ -255,6 +255,30 @@ def test_update_misaligned_labels_equal_aligned(km, n, k):
     assert torch.equal(n_a, n_m) and torch.equal(C_a, C_m)
 
 
+@pytest.mark.parametrize("n,k,batch", [(20_011, 300, 1), (2_200_011, 5_000, 1), (30_001, 200, 3), (70_001, 64, 1)])
+def test_update_out_of_range_labels_clamp(km, n, k, batch):
+    """Labels outside [0, K) handed to kmeans_update are a caller error with
+    unspecified results that must stay memory safe: the sort clamps each
+    such label to K - 1 (negative ones included), so the update equals, bit
+    for bit, the update of the clamped labels.  Shapes: one wide-digit pass,
+    the two-pass 16-bit sort, the segmented batched pass and one scanned
+    8-bit pass, each with a ragged last tile."""
+    X, C0, _, _ = _mixture(n, 32, k, "fp16", seed=n % 97 + k, batch=batch)
+    Xc = X.cuda() if batch > 1 else X[0].cuda()
+    C = C0.cuda() if batch > 1 else C0[0].cuda()
+    lab, _, _ = km.assign(Xc, C)
+    bad = torch.tensor([-1, -(2 ** 31), k, k + 5, 2 ** 31 - 1], dtype=torch.int32, device="cuda")
+    raw = lab.clone().reshape(-1)
+    idx = torch.arange(0, raw.numel(), 7, device="cuda")
+    raw[idx] = bad[torch.arange(idx.numel(), device="cuda") % bad.numel()]
+    clamped = torch.where((raw >= 0) & (raw < k), raw, torch.full_like(raw, k - 1))
+    C_r, n_r = km.update(Xc, raw.reshape(lab.shape), C)
+    C_c, n_c = km.update(Xc, clamped.reshape(lab.shape), C)
+    torch.cuda.synchronize()
+    assert torch.equal(n_r, n_c) and torch.equal(C_r, C_c)
+    assert int(n_r.sum()) == batch * n
+
+
 @pytest.mark.parametrize("n,k,batch", [(20_011, 257, 1), (50_000, 2048, 1), (30_001, 300, 2), (9_001, 290, 7)])
 def test_wide_digit_update(km, n, k, batch):
     """Keys of 9 to 11 bits (B*K from 257 to 2048) sort in one pass with a
