@@ -255,6 +255,24 @@ def test_update_misaligned_labels_equal_aligned(km, n, k):
     assert torch.equal(n_a, n_m) and torch.equal(C_a, C_m)
 
 
+@pytest.mark.parametrize("n", [2052 * 4096 - 5, 9_000_001])
+def test_update_scan_over_several_rounds(km, n):
+    """More than 2,048 tiles of 4,096 keys: the digit scan covers 2,048 tile
+    counts per round, so these take two rounds, with 16-byte loads (2,052
+    tiles) and with the per-count path (2,198 tiles, not a multiple of 4);
+    both passes of the 16-bit sort (K = 5,000) scan.  Counts exactly and
+    centroids within tolerance against the oracle."""
+    K = 5_000
+    X, C0, _, _ = _mixture(n, 16, K, "fp16", seed=n % 1009)
+    Xc, C = X[0].cuda(), C0[0].cuda()
+    lab, _, _ = km.assign(Xc, C)
+    C_new, counts = km.update(Xc, lab, C)
+    torch.cuda.synchronize()
+    err = H.check_update(H.decode(X[0], "fp16"), lab.cpu().numpy(), C.cpu().numpy(), C_new.cpu().numpy(),
+                         counts.cpu().numpy(), K, tag=f"n={n}")
+    print(f"n={n}: centroid rel err {err:.2e}")
+
+
 @pytest.mark.parametrize("n,k,batch", [(20_011, 300, 1), (2_200_011, 5_000, 1), (30_001, 200, 3), (70_001, 64, 1)])
 def test_update_out_of_range_labels_clamp(km, n, k, batch):
     """Labels outside [0, K) handed to kmeans_update are a caller error with
