@@ -174,6 +174,9 @@ constexpr int kSegRows = FKM_SEG_ROWS;
 constexpr int kSegRowsSmall = 128;  // chunk rows for small problems, so the level-1 grid still fills the chip
 constexpr int kSegGroup = 8;        // level-1 chunks per level-2 group
 // Rows per level-1 chunk for n sorted rows.
+static_assert((kSegRows & (kSegRows - 1)) == 0 && (kSegRowsSmall & (kSegRowsSmall - 1)) == 0 &&
+                  (kSegGroup & (kSegGroup - 1)) == 0,
+              "segment units are powers of two (levels 2 and 3 divide by shifting)");
 inline int seg_rows(int64_t n) { return n <= ((int64_t)1 << 21) ? kSegRowsSmall : kSegRows; }
 inline int64_t seg_chunks(int64_t n) { return (n + seg_rows(n) - 1) / seg_rows(n); }
 inline int64_t seg_groups(int64_t n) { return (seg_chunks(n) + kSegGroup - 1) / kSegGroup; }

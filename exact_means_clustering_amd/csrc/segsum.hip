@@ -32,8 +32,11 @@ namespace fkm {
 
 namespace {
 
-__device__ __forceinline__ int frag_slot(int64_t u, int64_t U, int64_t s) {
-  return (u == s / U && s != u * U) ? 1 : 0;
+// (Units are powers of two, U = 2^ulog, and positions are non-negative, so
+// divisions by U are shifts: a 64-bit division is a long instruction
+// sequence on the GPU.)
+__device__ __forceinline__ int frag_slot(int64_t u, int ulog, int64_t s) {
+  return (u == (s >> ulog) && s != (u << ulog)) ? 1 : 0;
 }
 
 // The fused centroid preparation of cluster k (means mode with o.chat):
@@ -42,8 +45,9 @@ template <class T, int D>
 __device__ __forceinline__ void fused_prep(const SegOut& o, int64_t k, int lane, const float (&c)[(D + 63) / 64]) {
   const float ss = prep_row<T, D>(c, reinterpret_cast<typename T::raw*>(o.chat) + k * D, lane);
   if (lane == 0) {
-    const int64_t b = k / o.K;
-    o.hb[b * o.Kp + (k - b * o.K)] = -0.5f * ss;
+    // B * K < 2^31, so a 32-bit division (a 64-bit one is a long sequence)
+    const uint32_t b = (uint32_t)k / o.K;
+    o.hb[(int64_t)b * o.Kp + ((uint32_t)k - b * o.K)] = -0.5f * ss;
   }
 }
 
@@ -379,6 +383,7 @@ __global__ __launch_bounds__(256) void seg_level2_kernel(const uint2* __restrict
                                                          double* __restrict__ gfrag) {
   constexpr int PER = (D + 63) / 64;
   const int64_t UG = U * kSegGroup;
+  const int ulog = __builtin_ctzll((unsigned long long)U);  // U is a power of two
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
   const int64_t g = blockIdx.x;
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(256) void seg_level2_kernel(const uint2* __restrict
     const bool valid = kk <= kl;
     const int64_t sv = valid ? off[kk] : 0, ev = valid ? off[kk + 1] : 0;
     // crosses a chunk edge (a segment inside one chunk was finished at level 1)
-    const bool cross = valid && sv < ev && (sv / U != (ev - 1) / U);
+    const bool cross = valid && sv < ev && ((sv >> ulog) != ((ev - 1) >> ulog));
     uint64_t all = __ballot(cross);
     // this wave's share: every 4th crossing segment in order
     uint64_t mask = 0;
@@ -412,10 +417,10 @@ __global__ __launch_bounds__(256) void seg_level2_kernel(const uint2* __restrict
       double acc[PER];
 #pragma unroll
       for (int q = 0; q < PER; ++q) acc[q] = 0.0;
-      const int64_t u0 = a / U, u1 = (z - 1) / U;
+      const int64_t u0 = a >> ulog, u1 = (z - 1) >> ulog;
 #pragma unroll 4
       for (int64_t u = u0; u <= u1; ++u) {
-        const float* fp = frag + (u * 2 + frag_slot(u, U, s)) * D;
+        const float* fp = frag + (u * 2 + frag_slot(u, ulog, s)) * D;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
           const int d = lane + 64 * q;
@@ -452,6 +457,7 @@ __global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint2* 
                                                                    const double* __restrict__ gfrag) {
   constexpr int PER = (D + 63) / 64;
   const int64_t UG = U * kSegGroup;
+  const int glog = __builtin_ctzll((unsigned long long)UG);  // UG is a power of two
   __shared__ double part[kL3Waves][PER * 64];
   __shared__ int64_t own_k[kL3Waves], own_s[kL3Waves], own_e[kL3Waves];
   const int lane = lane_id();
@@ -467,14 +473,14 @@ __global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint2* 
       e = off[kk + 1];
       if (s < gr0 && e <= gr1) k = kk;
     }
-    if (k >= 0 && g - s / UG < kL3Waves) {
+    if (k >= 0 && g - (s >> glog) < kL3Waves) {
       // short span: this wave alone, in group order
       double acc[PER];
 #pragma unroll
       for (int q = 0; q < PER; ++q) acc[q] = 0.0;
 #pragma unroll 4
-      for (int64_t gg = s / UG; gg <= g; ++gg) {
-        const double* gp = gfrag + (gg * 2 + frag_slot(gg, UG, s)) * D;
+      for (int64_t gg = s >> glog; gg <= g; ++gg) {
+        const double* gp = gfrag + (gg * 2 + frag_slot(gg, glog, s)) * D;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
           const int d = lane + 64 * q;
@@ -500,8 +506,8 @@ __global__ __launch_bounds__(kL3Waves * 64) void seg_level3_kernel(const uint2* 
 #pragma unroll
     for (int q = 0; q < PER; ++q) acc[q] = 0.0;
 #pragma unroll 4
-    for (int64_t gg = s / UG + w; gg <= g_end; gg += kL3Waves) {
-      const double* gp = gfrag + (gg * 2 + frag_slot(gg, UG, s)) * D;
+    for (int64_t gg = (s >> glog) + w; gg <= g_end; gg += kL3Waves) {
+      const double* gp = gfrag + (gg * 2 + frag_slot(gg, glog, s)) * D;
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const int d = lane + 64 * q;
