@@ -52,6 +52,13 @@ struct LabelSrc {
     return (uint32_t)b * K + lab;
   }
   __device__ __forceinline__ uint2 operator()(int64_t i) const { return make_uint2(key(labels[i], i), (uint32_t)i); }
+  // A segmented pass's tile lies inside one instance, whose key offset koff
+  // = b * K the tile already knows: the key is koff + the clamped label, with
+  // no per-element instance division.
+  __device__ __forceinline__ uint2 in_instance(int64_t i, uint32_t koff) const {
+    const uint32_t l = (uint32_t)labels[i];
+    return make_uint2(koff + (l < K ? l : K - 1), (uint32_t)i);
+  }
 };
 struct PairSrc {
   const uint2* kv;
@@ -229,7 +236,10 @@ __global__ __launch_bounds__(kT) void radix_hist_kernel(Src src, int64_t n, int 
 #pragma unroll
     for (int r = 0; r < kIPT; ++r) {
       const int64_t li = p.first + r * kT + t;
-      d[r] = li < p.lim ? ((src(p.row0 + li).x - p.koff) >> shift) & (R - 1) : R;
+      uint2 kv;
+      if constexpr (is_label_src<Src> && SEG) kv = li < p.lim ? src.in_instance(p.row0 + li, p.koff) : make_uint2(0u, 0u);
+      else kv = li < p.lim ? src(p.row0 + li) : make_uint2(0u, 0u);
+      d[r] = li < p.lim ? ((kv.x - p.koff) >> shift) & (R - 1) : R;
     }
   }
   // LDS atomics: the counts are exact integers, so their order is irrelevant.
@@ -416,7 +426,8 @@ __global__ __launch_bounds__(kT) void radix_scatter_kernel(Src src, int64_t n, i
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       const int64_t li = first + r * 64 + lane;
-      e[r] = li < p.lim ? src(p.row0 + li) : make_uint2(0u, 0u);
+      if constexpr (is_label_src<Src> && SEG) e[r] = li < p.lim ? src.in_instance(p.row0 + li, p.koff) : make_uint2(0u, 0u);
+      else e[r] = li < p.lim ? src(p.row0 + li) : make_uint2(0u, 0u);
     }
   }
 
