@@ -7,8 +7,9 @@
 // its slot while the compute stream assigns chunk c, sorts its labels and
 // adds its per-cluster sums into fp64 accumulators (chunk order fixed, so the
 // result is deterministic).  Labels of each chunk go back to the host on the
-// copy stream.  After the last chunk of an iteration the means are formed
-// once from the fp64 sums.
+// copy stream (in the last iteration, whose labels are the result).  After
+// the last chunk of an iteration the means are formed once from the fp64
+// sums.
 #include "kernels.h"
 #include "workspace.h"
 
@@ -195,8 +196,11 @@ extern "C" int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N,
       KS_HIP(hipEventRecord(r.done[sl], r.cs), "event record");
       KS_HIP(hipStreamWaitEvent(r.xs, r.done[sl], 0), "stream wait");
       if (int rc = mark(r.xs)) return rc;
-      KS_HIP(hipMemcpyAsync(labels_host + c * chunk, lslot[sl], (size_t)rows * 4, hipMemcpyDeviceToHost, r.xs),
-             "labels D2H copy");
+      // only the last iteration's labels are returned, so earlier iterations
+      // keep the copy stream for the points (their labels-out windows are empty)
+      if (t == iters - 1)
+        KS_HIP(hipMemcpyAsync(labels_host + c * chunk, lslot[sl], (size_t)rows * 4, hipMemcpyDeviceToHost, r.xs),
+               "labels D2H copy");
       if (int rc = mark(r.xs)) return rc;
       KS_HIP(hipEventRecord(r.freed[sl], r.xs), "event record");
     }

@@ -167,7 +167,8 @@ KM_API int kmeans_fit_streamed(const void* X_host, int32_t dtype, int64_t N, int
  * in issue order: iteration, chunk, then the start and end (ms, relative to
  * the fit's first event, from HIP events recorded on the copy and compute
  * streams) of the chunk's host-to-device copy, of its compute (assign, sort,
- * segment sums) and of its labels' device-to-host copy.  The first
+ * segment sums) and of its labels' device-to-host copy (only the last
+ * iteration copies labels; earlier iterations' windows are empty).  The first
  * min(cap, *count) rows go to `rows` (host, nullable when cap = 0) and
  * *count receives their number (0 if no streamed fit ran on this thread, or
  * if it had more than 16,384 chunk iterations, which record no timeline).
